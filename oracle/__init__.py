@@ -1,0 +1,154 @@
+"""fp64 CPU oracle for exact attention.
+
+TEST INFRASTRUCTURE ONLY.  The tests, the smoke check and the CPU-baseline
+leg of the benchmark may import this package; the GPU library and its Python
+binding never do, and nothing here imports them.
+
+Two independent implementations of the same plain definition live here:
+
+* ``attn_oracle.c`` (loaded through ctypes): row-by-row fp64 attention that
+  materialises each query row's scores, parallel over rows with OpenMP.  It
+  is the oracle the GPU path is compared with.
+* ``brute.py``: whole-matrix NumPy fp64 attention with an explicit boolean
+  mask, used only to check the C oracle on tiny inputs.
+
+The definition both follow is softmax(scale * Q K^T + mask) V with the
+natural-log logsumexp of each row («Оптимизация внимания Flash», Workflow 1,
+Steps 2 and 4; Workflow 2, Steps 2-3; «Что такое memory-efficient attention
+для long context на 8x H100?», section 2).  The header of ``attn_oracle.c``
+states the formula and the readings taken where the pages are silent.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "attn_oracle.c")
+LIBRARY = os.path.join(_HERE, "_attn_oracle.so")
+
+DTYPES = {"f16": 0, "fp16": 0, "float16": 0, "bf16": 1, "bfloat16": 1}
+
+_lib = None
+
+
+def compile_library(source: str = SOURCE, output: str = LIBRARY, extra_flags=()) -> str:
+    """Compile the C oracle with gcc into a shared library and return its path."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+           *extra_flags, "-o", output, source, "-lm"]
+    subprocess.run(cmd, check=True)
+    return output
+
+
+def build(force: bool = False) -> str:
+    """Build ``_attn_oracle.so`` next to its source if missing or stale."""
+    stale = (not os.path.exists(LIBRARY)
+             or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE))
+    if force or stale:
+        compile_library()
+    return LIBRARY
+
+
+def _bind(lib):
+    u16p = ctypes.POINTER(ctypes.c_uint16)
+    f64p = ctypes.POINTER(ctypes.c_double)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    lib.oracle_attn.restype = ctypes.c_int
+    lib.oracle_attn.argtypes = [u16p, u16p, u16p, ctypes.c_int,
+                                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                i64p, ctypes.c_int64, f64p, f64p, ctypes.c_int]
+    lib.oracle_decode.restype = None
+    lib.oracle_decode.argtypes = [u16p, f64p, ctypes.c_int64, ctypes.c_int]
+    lib.oracle_resolve_scale.restype = ctypes.c_float
+    lib.oracle_resolve_scale.argtypes = [ctypes.c_float, ctypes.c_int]
+    lib.oracle_visible.restype = ctypes.c_int
+    lib.oracle_visible.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int]
+    return lib
+
+
+def load_library(path: str):
+    """Load a compiled oracle library (the default one or a test-built variant)."""
+    return _bind(ctypes.CDLL(path))
+
+
+def _default_lib():
+    global _lib
+    if _lib is None:
+        _lib = load_library(build())
+    return _lib
+
+
+def _ptr(a, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _bits(a) -> np.ndarray:
+    """16-bit patterns of a float16/bfloat16 torch tensor or a uint16/float16 array."""
+    if hasattr(a, "detach"):  # torch tensor, CPU
+        import torch
+        a = a.detach().cpu().contiguous().view(torch.int16).numpy()
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float16:
+        a = a.view(np.uint16)
+    if a.dtype == np.int16:
+        a = a.view(np.uint16)
+    if a.dtype != np.uint16:
+        raise TypeError(f"expected 16-bit float patterns, got {a.dtype}")
+    return a
+
+
+def decode(bits, dtype: str, lib=None) -> np.ndarray:
+    """Exact fp64 values of 16-bit float patterns (same shape)."""
+    lib = lib or _default_lib()
+    b = _bits(bits)
+    out = np.empty(b.shape, np.float64)
+    lib.oracle_decode(_ptr(b, ctypes.c_uint16), _ptr(out, ctypes.c_double), b.size, DTYPES[dtype])
+    return out
+
+
+def resolve_scale(scale: float, d: int, lib=None) -> float:
+    """The fp32 scale the definition uses: ``scale`` or, if <= 0/NaN, fp32(1/sqrt(d))."""
+    lib = lib or _default_lib()
+    return float(lib.oracle_resolve_scale(float(scale), int(d)))
+
+
+def attention(q, k, v, dtype: str, causal: bool, window: int = -1, scale: float = 0.0,
+              rows=None, threads: int = 0, lib=None):
+    """Exact attention of 16-bit inputs in fp64.
+
+    q: [B,H,L,d]; k, v: [B,H_kv,L,d] (torch tensors or uint16 arrays of bit
+    patterns).  ``rows``: optional flat row ids (b*H + h)*L + i; when given,
+    the result holds those rows only, in that order.
+    Returns (out, lse): fp64 [B,H,L,d] and [B,H,L], or [n, d] and [n].
+    """
+    lib = lib or _default_lib()
+    qb, kb, vb = _bits(q), _bits(k), _bits(v)
+    B, H, L, d = qb.shape
+    H_kv = kb.shape[1]
+    if kb.shape != (B, H_kv, L, d) or vb.shape != kb.shape:
+        raise ValueError(f"shape mismatch q{qb.shape} k{kb.shape} v{vb.shape}")
+    if rows is None:
+        n = B * H * L
+        rows_arr = None
+        rows_ptr = None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        n = rows_arr.size
+        if n and (rows_arr.min() < 0 or rows_arr.max() >= B * H * L):
+            raise ValueError("row id out of range")
+        rows_ptr = _ptr(rows_arr, ctypes.c_int64)
+    out = np.zeros((n, d), np.float64)
+    lse = np.zeros((n,), np.float64)
+    st = lib.oracle_attn(_ptr(qb, ctypes.c_uint16), _ptr(kb, ctypes.c_uint16), _ptr(vb, ctypes.c_uint16),
+                         DTYPES[dtype], B, H, H_kv, L, d, int(bool(causal)), int(window), float(scale),
+                         rows_ptr, n, _ptr(out, ctypes.c_double), _ptr(lse, ctypes.c_double),
+                         int(threads))
+    if st != 0:
+        raise ValueError(f"oracle_attn failed with status {st}")
+    if rows is None:
+        return out.reshape(B, H, L, d), lse.reshape(B, H, L)
+    return out, lse

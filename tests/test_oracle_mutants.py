@@ -1,0 +1,51 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each case copies the oracle's C source, changes one line into a plausible
+mistake (a dropped term, a wrong sign or bound, a wrong index or operand),
+compiles the copy into a temporary directory and runs the pins against it.
+At least one pin must fail for every mistake.  Runs on the CPU only.
+"""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+
+MUTANTS = {
+    "causal_excludes_diagonal": ("if (causal && j > i)", "if (causal && j >= i)"),
+    "window_off_by_one": ("if (i - j > window)", "if (i - j >= window)"),
+    "window_ignores_right_side": ("if (!causal && j - i > window)", "if (0 && j - i > window)"),
+    "gqa_interleaved_heads": ("return h / (H / H_kv);", "return h % H_kv;"),
+    "lse_without_max": ("lse[t] = m + log(l);", "lse[t] = log(l);"),
+    "scale_dropped": ("s[j] = sc * dot;", "s[j] = dot;"),
+    "key_transposed": ("dot += qd[c] * kd[j * d + c];", "dot += qd[c] * kd[c * L + j];"),
+    "value_row_reversed": ("acc[c] += p * vd[j * d + c];", "acc[c] += p * vd[(L - 1 - j) * d + c];"),
+    "no_normalisation": ("out[t * d + c] = acc[c] / l;", "out[t * d + c] = acc[c];"),
+    "f16_subnormal_exponent": ("mag = ldexp((double)frac, -24);", "mag = ldexp((double)frac, -25);"),
+    "f16_bias": ("expo - 25); /*", "expo - 24); /*"),
+    "bf16_shift": ("(uint32_t)bits << 16;", "(uint32_t)bits << 15;"),
+    "default_scale_wrong": ("return (float)(1.0 / sqrt((double)d));", "return (float)(1.0 / (double)d);"),
+    "max_not_subtracted_from_lse_side": ("double p = exp(s[j] - m);", "double p = exp(s[j]);"),
+    "sum_over_one_row_only": ("l += p;", "l = p;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(oracle.SOURCE).read()
+    assert src.count(old) == 1, f"mutation anchor not found once: {old!r}"
+    path = os.path.join(tmp_path, "mutant.c")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    lib = oracle.load_library(oracle.compile_library(path, os.path.join(tmp_path, "mutant.so")))
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError) as exc:
+            caught.append(pin.__name__)
+            if len(caught) >= 1:
+                break
+    assert caught, f"no pin caught the planted mistake {name}"

@@ -1,0 +1,197 @@
+"""Benchmark of the exact attention forward on one MI355X.
+
+One step = one attn_fwd call over the whole workload (every query row of
+every head).  Default workload: causal attention, B=1, H=4, L=131072, d=64,
+fp16, scale 1/8 -- the longest length of the pages' length sweep at 4 heads.
+Prints ONE JSON line with throughput in TFLOP/s (algorithmic FLOPs: 4*d per
+visible (query, key) pair, so causal counts only the unmasked half), the
+roofline of the kernel against the dense fp16 MFMA peak, and a CPU baseline:
+the fp64 oracle timed on a bounded sample of the same workload's rows (whose
+GPU outputs are also checked against it).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--sweep]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import exact_io_aware_25_amd as attn  # noqa: E402
+from synth import WORKLOADS, workload_inputs  # noqa: E402
+
+MFMA_PEAK_F16_TFLOPS = 2516.6   # MI355X dense fp16/bf16: 256 CU x 4096 FLOP/clk x 2.4 GHz
+HBM_PEAK_GBS = 8000.0
+METRIC = "causal attn fwd TFLOP/s @ L=128k,H=4,d=64 fp16; % of MFMA peak"
+DEFAULT_WORKLOAD = "causal_128k_h4"
+
+
+def visible_pairs(L: int, causal: bool, window: int) -> int:
+    """Number of (query, key) pairs the mask leaves visible in one head."""
+    i = np.arange(L, dtype=np.int64)
+    lo = np.zeros(L, np.int64) if window < 0 else np.maximum(0, i - window)
+    if causal:
+        hi = i + 1
+    else:
+        hi = np.full(L, L, np.int64) if window < 0 else np.minimum(L, i + window + 1)
+    return int((hi - lo).sum())
+
+
+def row_visible(i: np.ndarray, L: int, causal: bool, window: int) -> np.ndarray:
+    lo = np.zeros_like(i) if window < 0 else np.maximum(0, i - window)
+    if causal:
+        hi = i + 1
+    else:
+        hi = np.full_like(i, L) if window < 0 else np.minimum(L, i + window + 1)
+    return hi - lo
+
+
+def algorithmic_flops(w) -> float:
+    return 4.0 * w.d * w.B * w.H * visible_pairs(w.L, w.causal, w.window)
+
+
+def algorithmic_bytes(w) -> float:
+    """One read of q, k, v and one write of out (16-bit) and lse (fp32)."""
+    return 2.0 * w.B * w.L * w.d * (2 * w.H + 2 * w.H_kv) + 4.0 * w.B * w.H * w.L
+
+
+def time_workload(w, steps: int, warmup: int):
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in workload_inputs(w))
+    torch.cuda.synchronize()
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev)
+    torch.cuda.reset_peak_memory_stats(dev)
+    base = torch.cuda.memory_allocated(dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        attn.forward(q, k, v, causal=w.causal, window=w.window, scale=w.scale, out=out, lse=lse,
+                     stream=stream)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        attn.forward(q, k, v, causal=w.causal, window=w.window, scale=w.scale, out=out, lse=lse,
+                     stream=stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(stop) / steps
+    peak_mem = torch.cuda.max_memory_allocated(dev)
+    return dict(ms=ms, wall_s=wall, out=out, lse=lse, inputs=(q, k, v), peak_mem=peak_mem,
+                extra_mem=peak_mem - base)
+
+
+def cpu_baseline(w, out, lse, inputs, budget_s: float = 15.0, seed: int = 7):
+    """Time the fp64 oracle on a seeded sample of rows for about `budget_s`
+    seconds; return its throughput in the metric's unit and the GPU-vs-oracle
+    error on those rows."""
+    import oracle
+    q, k, v = (t.cpu() for t in inputs)
+    threads = len(os.sched_getaffinity(0))
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        threads = min(threads, int(os.environ["OMP_NUM_THREADS"]))
+    rng = np.random.default_rng(seed)
+    n_total = w.B * w.H * w.L
+    order = rng.permutation(n_total)
+    done, flops, elapsed = 0, 0.0, 0.0
+    err_o, err_l = 0.0, 0.0
+    flat_o = out.reshape(-1, w.d)
+    flat_l = lse.reshape(-1)
+    batch = 64
+    while elapsed < budget_s and done < n_total:
+        rows = np.sort(order[done:done + batch])
+        t0 = time.perf_counter()
+        ro, rl = oracle.attention(q, k, v, w.dtype, w.causal, w.window, w.scale, rows=rows, threads=threads)
+        elapsed += time.perf_counter() - t0
+        flops += 4.0 * w.d * float(row_visible(rows % w.L, w.L, w.causal, w.window).sum())
+        idx = torch.from_numpy(rows)
+        go = flat_o[idx.to(flat_o.device)].double().cpu().numpy()
+        gl = flat_l[idx.to(flat_l.device)].double().cpu().numpy()
+        err_o = max(err_o, float(np.abs(go - ro).max()))
+        err_l = max(err_l, float(np.abs(gl - rl).max()))
+        done += len(rows)
+        batch = min(4096, batch * 2)
+    return dict(value=flops / elapsed / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
+                sample=f"{done} seeded random query rows of {n_total} ({w.name}), "
+                       f"{elapsed:.1f} s of fp64 oracle time, {flops:.3e} algorithmic FLOPs",
+                parity_max_abs_o=err_o, parity_max_abs_lse=err_l)
+
+
+def roofline_block(w, ms):
+    flops = algorithmic_flops(w)
+    achieved = flops / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_PEAK_F16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_F16_TFLOPS, 4), "traffic": None}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time every workload and print one extra JSON line each (to stderr)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the kernel shards over (batch, head) with no exchange, so N GPUs run N independent "
+              "copies).", file=sys.stderr)
+        sys.exit(2)
+
+    w = WORKLOADS[args.workload]
+    attn.library()
+    r = time_workload(w, args.steps, args.warmup)
+    flops = algorithmic_flops(w)
+    tflops = flops / (r["ms"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: seeded iid N(0,1) q, k, v rounded to the 16-bit type",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.H_kv, "L": w.L, "d": w.d,
+                   "causal": w.causal, "window": w.window, "scale": w.scale,
+                   "algorithmic_flops": flops, "pct_of_mfma_peak": round(100 * tflops / MFMA_PEAK_F16_TFLOPS, 2),
+                   "peak_mem_bytes": r["peak_mem"], "algorithmic_bytes": algorithmic_bytes(w)},
+        "roofline": roofline_block(w, r["ms"]),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, r["out"], r["lse"], r["inputs"], args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+    if args.sweep:
+        for name, ws in WORKLOADS.items():
+            rs = time_workload(ws, max(5, args.steps), 3)
+            f = algorithmic_flops(ws)
+            print(json.dumps({"workload": name, "ms": round(rs["ms"], 4),
+                              "tflops": round(f / (rs["ms"] * 1e-3) / 1e12, 2),
+                              "pct_peak": round(100 * f / (rs["ms"] * 1e-3) / 1e12 / MFMA_PEAK_F16_TFLOPS, 2),
+                              "peak_mem_bytes": rs["peak_mem"], "L": ws.L}), file=sys.stderr, flush=True)
+            del rs
+            torch.cuda.empty_cache()
+
+
+if __name__ == "__main__":
+    main()

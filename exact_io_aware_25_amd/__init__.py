@@ -1,0 +1,129 @@
+"""Exact IO-aware attention forward for AMD MI355X (gfx950).
+
+A thin ctypes binding over the C ABI declared in ``include/attn.h``.  The
+names match the C entry points; this module only marshals arguments.  Every
+step of the computation runs in the HIP kernels of ``libattn_gfx950.so``;
+there is no fallback: if the library is missing, every call raises.
+
+``forward`` is a convenience for PyTorch users: it checks the tensors,
+allocates ``out`` and ``lse`` with torch on the inputs' device and launches
+on torch's current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_HERE, "libattn_gfx950.so")
+
+ATTN_OK = 0
+ATTN_ERR_NULL = 1
+ATTN_ERR_SHAPE = 2
+ATTN_ERR_HEAD_DIM = 3
+ATTN_ERR_WINDOW = 4
+ATTN_ERR_ALIAS = 5
+ATTN_ERR_LAUNCH = 6
+ATTN_ERR_SIZE = 7
+ATTN_ERR_FLAG = 8
+ATTN_ERR_SCALE = 9
+ATTN_ERR_ALIGN = 10
+
+EXPORTS = ("attn_fwd", "attn_fwd_bf16", "attn_status_string", "attn_resolve_scale")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    """A non-zero status from the library."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+def library():
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            raise RuntimeError(
+                f"{LIBRARY} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+        lib = ctypes.CDLL(LIBRARY)
+        sig = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+               ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+               ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p]
+        for name in ("attn_fwd", "attn_fwd_bf16"):
+            fn = getattr(lib, name)
+            fn.restype = ctypes.c_int
+            fn.argtypes = sig
+        lib.attn_status_string.restype = ctypes.c_char_p
+        lib.attn_status_string.argtypes = [ctypes.c_int]
+        lib.attn_resolve_scale.restype = ctypes.c_float
+        lib.attn_resolve_scale.argtypes = [ctypes.c_float, ctypes.c_int]
+        _lib = lib
+    return _lib
+
+
+def attn_fwd(q, k, v, out, lse, B, H, H_kv, L, d, causal, window, scale, stream) -> int:
+    """fp16 entry point; pointers are integer device addresses, stream a hipStream_t address."""
+    return library().attn_fwd(q, k, v, out, lse, B, H, H_kv, L, d, causal, window, scale, stream)
+
+
+def attn_fwd_bf16(q, k, v, out, lse, B, H, H_kv, L, d, causal, window, scale, stream) -> int:
+    """bf16 entry point; same arguments as ``attn_fwd``."""
+    return library().attn_fwd_bf16(q, k, v, out, lse, B, H, H_kv, L, d, causal, window, scale, stream)
+
+
+def attn_status_string(status: int) -> str:
+    return library().attn_status_string(int(status)).decode()
+
+
+def attn_resolve_scale(scale: float, d: int) -> float:
+    return float(library().attn_resolve_scale(float(scale), int(d)))
+
+
+def forward(q, k, v, causal: bool = False, window: int = -1, scale=None, out=None, lse=None,
+            stream=None):
+    """Attention of torch tensors q [B,H,L,d], k and v [B,H_kv,L,d] (fp16 or bf16, on the GPU).
+
+    Returns (out [B,H,L,d] of q's dtype, lse [B,H,L] fp32).  ``scale=None``
+    selects 1/sqrt(d).  ``out``/``lse`` may be given to write into existing
+    tensors.  Launches on ``stream`` (default: torch's current stream).
+    """
+    import torch
+
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D: [B, H, L, d] and [B, H_kv, L, d]")
+    if q.dtype not in (torch.float16, torch.bfloat16) or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype, float16 or bfloat16")
+    if not (q.is_cuda and k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on the same GPU device")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, L, d = q.shape
+    H_kv = k.shape[1]
+    if tuple(k.shape) != (B, H_kv, L, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch: q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
+    if (tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or not out.is_contiguous()
+            or out.device != q.device):
+        raise ValueError("out must be a contiguous tensor like q")
+    if (tuple(lse.shape) != (B, H, L) or lse.dtype != torch.float32 or not lse.is_contiguous()
+            or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, L]")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    fn = attn_fwd if q.dtype == torch.float16 else attn_fwd_bf16
+    with torch.cuda.device(q.device):
+        status = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                    B, H, H_kv, L, d, int(bool(causal)), int(window),
+                    0.0 if scale is None else float(scale), stream.cuda_stream)
+    if status != ATTN_OK:
+        exc = ValueError if status in (1, 2, 3, 4, 5, 8, 9, 10) else AttnError
+        msg = attn_status_string(status)
+        raise exc(msg) if exc is ValueError else exc(status, msg)
+    return out, lse

@@ -1,0 +1,105 @@
+/*
+ * attn.h -- C ABI of the exact attention forward pass for AMD MI355X (gfx950).
+ *
+ * The operation is exact scaled-dot-product attention computed the
+ * IO-aware way: Q, K and V are streamed through on-chip tiles, the softmax is
+ * accumulated online, and only O and its logsumexp are written, so device
+ * memory stays linear in the sequence length («Что такое memory-efficient
+ * attention для long context на 8x H100?», section 2, "FlashAttention-3:
+ * IO-aware attention").  The result is the plain definition (the same page
+ * calls the method exact):
+ *
+ *   O[b,h,i,:] = sum_{j in V(i)} softmax_j(scale * q[b,h,i,:] . k[b,g,j,:]) * v[b,g,j,:]
+ *   lse[b,h,i] = ln sum_{j in V(i)} exp(scale * q[b,h,i,:] . k[b,g,j,:])
+ *
+ * with g = h / (H / H_kv): query heads form H_kv contiguous groups that share
+ * one K/V head (grouped/multi-query attention, «Оптимизация внимания Flash»,
+ * Workflow 2, Step 3).  The visible keys V(i) of query row i are
+ *   causal = 1:  j <= i                          (Quick start; Workflow 2, Step 2)
+ *   window >= 0: i - window <= j, and j <= i + window when causal = 0
+ *                (sliding window, Workflow 2, Step 3: a (left, right) pair
+ *                with -1 for "no limit"; one int covers both sides here, and
+ *                the causal flag forces the right side to 0)
+ *   window = -1: no window.
+ * The diagonal key is always visible, so no row is empty.
+ *
+ * Layout (all contiguous, row-major, no strides):
+ *   q, out : [B, H,    L, d]   16-bit floats (fp16 for attn_fwd, bf16 for attn_fwd_bf16)
+ *   k, v   : [B, H_kv, L, d]   same 16-bit type
+ *   lse    : [B, H,    L]      fp32, natural log
+ * d must be 64 or 128.  The pages' inputs are fp16/bf16 only («Оптимизация
+ * внимания Flash», Common issues: fp32 is not supported by the fast path).
+ *
+ * scale: used as given when finite and > 0; when <= 0 or NaN the automatic
+ * scale 1/sqrt(d) is used (Workflow 2, Step 2: softmax_scale=None), as the
+ * fp32 value nearest to it.  An infinite scale is rejected.
+ *
+ * Ownership and behaviour:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller, who
+ *     allocates and frees it.  The library allocates no device memory, keeps
+ *     no state between calls except a once-filled table of device properties,
+ *     and never synchronises.
+ *   - stream is a hipStream_t (NULL = the default stream).  The call enqueues
+ *     the kernel on it and returns; results are ready once the stream has
+ *     reached that point.  Calls on different streams may run concurrently.
+ *   - Arguments are validated before any HIP call, so an invalid call has no
+ *     effect on the device and can be made without a GPU.
+ *   - B = 0 or L = 0 is an empty problem: nothing is launched, ATTN_OK is
+ *     returned, and the pointers may be NULL.
+ *   - out and lse must not overlap each other or q, k, v (q, k and v may
+ *     overlap one another: they are only read).
+ *   - q, k, v and out must be 16-byte aligned, lse 4-byte aligned.
+ *   - The grid is launched on the device that is current on the calling
+ *     thread; the pointers and the stream must belong to it.
+ *   - Errors during kernel execution surface at the caller's next
+ *     synchronisation with the stream, as for any HIP kernel.
+ */
+#ifndef EXACT_IO_AWARE_ATTN_H
+#define EXACT_IO_AWARE_ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by the entry points. */
+enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,     /* a tensor pointer is NULL for a non-empty problem              */
+    ATTN_ERR_SHAPE = 2,    /* B < 0, L < 0, H < 1, H_kv < 1, or H not a multiple of H_kv   */
+    ATTN_ERR_HEAD_DIM = 3, /* d is neither 64 nor 128                                       */
+    ATTN_ERR_WINDOW = 4,   /* window < -1                                                   */
+    ATTN_ERR_ALIAS = 5,    /* out or lse overlaps another tensor                            */
+    ATTN_ERR_LAUNCH = 6,   /* the HIP runtime refused the launch (no gfx950 device, ...)    */
+    ATTN_ERR_SIZE = 7,     /* a tensor or the grid is too large to index                    */
+    ATTN_ERR_FLAG = 8,     /* causal is neither 0 nor 1                                     */
+    ATTN_ERR_SCALE = 9,    /* scale is +/- infinity                                         */
+    ATTN_ERR_ALIGN = 10    /* q, k, v or out not 16-byte aligned, or lse not 4-byte aligned */
+};
+
+/*
+ * Exact attention forward for fp16 (IEEE binary16) q, k, v and out.
+ * Computes out and lse as defined above for all B*H*L query rows.
+ * Returns an attn_status; ATTN_OK means the kernel was enqueued.
+ */
+int attn_fwd(const void *q, const void *k, const void *v, void *out, float *lse,
+             int B, int H, int H_kv, int L, int d, int causal, int window, float scale,
+             void *stream);
+
+/* The same operation for bfloat16 q, k, v and out (lse stays fp32). */
+int attn_fwd_bf16(const void *q, const void *k, const void *v, void *out, float *lse,
+                  int B, int H, int H_kv, int L, int d, int causal, int window, float scale,
+                  void *stream);
+
+/* A static, human-readable name for a status code (never NULL). */
+const char *attn_status_string(int status);
+
+/* The fp32 scale the kernels use for a given scale argument and head size:
+ * `scale` itself when finite and > 0, else the fp32 value nearest 1/sqrt(d).
+ * Host-only; makes no HIP call. */
+float attn_resolve_scale(float scale, int d);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_IO_AWARE_ATTN_H */

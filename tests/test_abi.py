@@ -1,0 +1,94 @@
+"""The C-ABI library loads, exports what include/attn.h declares, and rejects
+bad arguments before any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_io_aware_25_amd as attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+# distinct fake device addresses, 1 MiB apart, never dereferenced
+Q, K, V, O, LSE = (0x10000000 + i * (1 << 20) for i in range(5))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == sorted(attn.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(attn.LIBRARY)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_codes_match_header():
+    text = open(HEADER).read()
+    codes = dict((n, int(v)) for n, v in re.findall(r"\b(ATTN_\w+)\s*=\s*(\d+)", text))
+    for name, value in codes.items():
+        assert getattr(attn, name) == value, name
+    for value in codes.values():
+        assert attn.attn_status_string(value) not in ("", "unknown status")
+    assert attn.attn_status_string(12345) == "unknown status"
+
+
+def call(fn=attn.attn_fwd, q=Q, k=K, v=V, o=O, lse=LSE, B=1, H=4, H_kv=2, L=256, d=64,
+         causal=1, window=-1, scale=0.125):
+    return fn(q, k, v, o, lse, B, H, H_kv, L, d, causal, window, scale, None)
+
+
+@pytest.mark.parametrize("fn", [attn.attn_fwd, attn.attn_fwd_bf16])
+def test_argument_errors(fn):
+    assert call(fn, q=0) == attn.ATTN_ERR_NULL
+    assert call(fn, lse=0) == attn.ATTN_ERR_NULL
+    assert call(fn, H=3, H_kv=2) == attn.ATTN_ERR_SHAPE
+    assert call(fn, H=0, H_kv=1) == attn.ATTN_ERR_SHAPE
+    assert call(fn, H_kv=0) == attn.ATTN_ERR_SHAPE
+    assert call(fn, B=-1) == attn.ATTN_ERR_SHAPE
+    assert call(fn, L=-5) == attn.ATTN_ERR_SHAPE
+    for d in (0, 32, 96, 256):
+        assert call(fn, d=d) == attn.ATTN_ERR_HEAD_DIM
+    assert call(fn, window=-2) == attn.ATTN_ERR_WINDOW
+    assert call(fn, causal=2) == attn.ATTN_ERR_FLAG
+    assert call(fn, causal=-1) == attn.ATTN_ERR_FLAG
+    assert call(fn, scale=float("inf")) == attn.ATTN_ERR_SCALE
+    assert call(fn, scale=float("-inf")) == attn.ATTN_ERR_SCALE
+    assert call(fn, o=Q) == attn.ATTN_ERR_ALIAS                 # out is q
+    assert call(fn, o=K + 64) == attn.ATTN_ERR_ALIAS            # out inside k
+    assert call(fn, lse=O + 1024) == attn.ATTN_ERR_ALIAS        # lse inside out
+    assert call(fn, lse=V) == attn.ATTN_ERR_ALIAS
+    assert call(fn, L=1 << 30, H=1 << 12, H_kv=1) == attn.ATTN_ERR_SIZE
+    assert call(fn, q=Q + 8) == attn.ATTN_ERR_ALIGN
+    assert call(fn, o=O + 2) == attn.ATTN_ERR_ALIGN
+    assert call(fn, lse=LSE + 2) == attn.ATTN_ERR_ALIGN
+
+
+@pytest.mark.parametrize("fn", [attn.attn_fwd, attn.attn_fwd_bf16])
+def test_empty_problems_return_ok_without_launching(fn):
+    assert call(fn, q=0, k=0, v=0, o=0, lse=0, B=0) == attn.ATTN_OK
+    assert call(fn, q=0, k=0, v=0, o=0, lse=0, L=0) == attn.ATTN_OK
+
+
+def test_resolve_scale():
+    import numpy as np
+    assert attn.attn_resolve_scale(0.0, 64) == 0.125
+    assert attn.attn_resolve_scale(float("nan"), 128) == float(np.float32(1 / np.sqrt(128.0)))
+    assert attn.attn_resolve_scale(-3.0, 128) == float(np.float32(1 / np.sqrt(128.0)))
+    assert attn.attn_resolve_scale(0.3, 64) == float(np.float32(0.3))
+
+
+def test_binding_does_not_import_the_oracle():
+    import sys
+    src = open(os.path.join(ROOT, "exact_io_aware_25_amd", "__init__.py")).read()
+    assert "oracle" not in src.replace("no fallback", "")
+    hip = open(os.path.join(ROOT, "exact_io_aware_25_amd", "csrc", "attn_fwd.hip")).read()
+    assert "oracle" not in hip

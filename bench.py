@@ -145,6 +145,9 @@ def main():
                     help="also time every workload and print one extra JSON line each (to stderr)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before timing, run one plain device copy of this many MiB (a reference "
+                         "kernel of known traffic for scaling profiler byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -155,6 +158,14 @@ def main():
 
     w = WORKLOADS[args.workload]
     attn.library()
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 2
+        src = torch.ones(n, dtype=torch.float16, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     r = time_workload(w, args.steps, args.warmup)
     flops = algorithmic_flops(w)
     tflops = flops / (r["ms"] * 1e-3) / 1e12

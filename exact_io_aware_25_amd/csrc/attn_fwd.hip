@@ -33,6 +33,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "attn.h"
 
@@ -49,7 +50,6 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = 32;
 constexpr int kBlockQ = kRowsPerWave * kWaves;  // query rows per workgroup
 constexpr int kBlockK = 64;                     // keys per K/V tile
-constexpr int kPad = 8;                         // 16 bytes of padding per LDS row
 
 template <typename T> struct Vec8;
 template <> struct Vec8<_Float16> { typedef f16x8 type; };
@@ -96,20 +96,82 @@ __device__ __forceinline__ bool visible(int i, int j, int L, int window)
     return true;
 }
 
+// XOR swizzles of the 16-byte units of each LDS tile row (tiles are not
+// padded).  A row of D 16-bit values has D/8 units; unit u of row r is stored
+// at unit u ^ f(r).  The functions are chosen so that both reads are free of
+// bank conflicts whether the LDS serves 8 lanes x 16 bytes (32 banks) or 16
+// lanes x 16 bytes (64 banks) per cycle:
+//  * K is read 16 bytes per lane from the 16 rows k_row_for_lane(0..15) of a
+//    32-row block, all at the same logical unit: f must be a bijection on row
+//    bits {0,1,3} (the first 8 of those rows) and on bits {1,2,3} for a fixed
+//    bit 0 (16 rows over two 128-byte halves);
+//  * V is read 8 bytes per lane by the transposing load, four consecutive rows
+//    at a time with two (16 lanes) or four (32 lanes) consecutive units per
+//    row: f must move the unit pair, and for 32 lanes the unit quad, of each
+//    of the four rows to a different place.
+template <int D> __device__ __forceinline__ int k_swizzle(int row)
+{
+    const int b0 = row & 1, b1 = (row >> 1) & 1, b2 = (row >> 2) & 1, b3 = (row >> 3) & 1;
+    return (b0 ^ b2) | (b1 << 1) | (b3 << 2) | (D == 128 ? (b2 << 3) : 0);
+}
+template <int D> __device__ __forceinline__ int v_swizzle(int row)
+{
+    const int c = row & 3;
+    return (c << 1) | (D == 128 ? ((c & 1) << 3) : 0);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Transposing 8-byte LDS read: within each group of 16 lanes, lane 4a+b gets
+// element b of the 8-byte chunks addressed by lanes a, a+4, a+8 and a+12.
+__device__ __forceinline__ s16x4 lds_read_tr16(const void *generic_lds_ptr)
+{
+    auto p = (__attribute__((address_space(3))) char *)(generic_lds_ptr);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p);
+}
+
+__device__ __forceinline__ float half_swap_max(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x)
+{
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float sum8(f16x8 v, float acc)
+{
+    const f16x2 one = {1, 1};
+    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
+    return __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
+}
+
+// Rescale threshold of the online softmax, in log2 units: the reference
+// maximum of a row is only moved when a new score exceeds it by more than
+// this, so softmax weights stay <= 2^8 (well inside fp16 and fp32 range) and
+// the accumulator rescale is skipped on almost every tile.  The result is
+// the same exact softmax: any reference value cancels between O and the sum.
+constexpr float kRescaleLog2 = 8.0f;
+
 template <typename T, int D, bool CAUSAL, bool WINDOW>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p)
 {
     typedef typename Vec8<T>::type vec8;
-    constexpr int KS = D + kPad;        // K tile row stride (elements)
-    constexpr int VS = kBlockK + kPad;  // V^T tile row stride (elements)
-    constexpr int kTileK = kBlockK * KS;
-    constexpr int kTileV = D * VS;
-    constexpr int kChunks = kBlockK * D / 8 / kThreads;  // 16-byte chunks per thread per tile
-    constexpr int kDSteps = D / 16;     // k-steps of the first product
-    constexpr int kDBlocks = D / 32;    // 32-row blocks of O^T
+    constexpr int kRowBytes = 2 * D;                      // one K or V row in LDS
+    constexpr int kTileBytes = kBlockK * kRowBytes;       // one K or V tile
+    constexpr int kUnits = D / 8;                         // 16-byte units per row
+    constexpr int kChunks = kBlockK * kUnits / kThreads;  // units per thread per tile
+    constexpr int kDSteps = D / 16;                       // k-steps of the first product
+    constexpr int kDBlocks = D / 32;                      // 32-row blocks of O^T
 
-    __shared__ __attribute__((aligned(16))) T lds_k[2][kTileK];
-    __shared__ __attribute__((aligned(16))) T lds_v[2][kTileV];
+    // [stage][K | V] tiles
+    __shared__ __attribute__((aligned(16))) char lds[2][2][kTileBytes];
 
     const int tid = threadIdx.x;
     const int wave = tid / 64;
@@ -159,11 +221,33 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p)
             qf[s] = vec8{};
     }
 
+    // ---- per-lane LDS byte offsets (swizzled), fixed for the whole pass
+    const int krow = k_row_for_lane(l32);
+    int koff[kDSteps];
+#pragma unroll
+    for (int ds = 0; ds < kDSteps; ++ds)
+        koff[ds] = krow * kRowBytes + 16 * ((2 * ds + hi) ^ k_swizzle<D>(krow));
+    const int tr_row = 8 * (lane >> 5) + ((lane >> 2) & 3);  // + 16*ks + 4*r
+    const int tr_unit = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    int voff[kDBlocks];
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db)
+        voff[db] = tr_row * kRowBytes + 16 * ((4 * db + tr_unit) ^ v_swizzle<D>(tr_row)) + 8 * (lane & 1);
+    int st_k[kChunks], st_v[kChunks];
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+        const int chunk = tid + c * kThreads;
+        const int row = chunk / kUnits, unit = chunk % kUnits;
+        st_k[c] = row * kRowBytes + 16 * (unit ^ k_swizzle<D>(row));
+        st_v[c] = row * kRowBytes + 16 * (unit ^ v_swizzle<D>(row));
+    }
+
     f32x16 acc_o[kDBlocks];
 #pragma unroll
     for (int i = 0; i < kDBlocks; ++i) acc_o[i] = f32x16{};
-    float m_run = -INFINITY;  // running max of scale*log2(e)*s over keys seen
-    float l_run = 0.f;        // running sum of exp2 weights, this lane's half of the keys
+    float m_run = -INFINITY;  // reference max of scale*log2(e)*s (log2 domain)
+    float neg_m = 0.f;        // -m_run, or 0 while m_run is -inf
+    float l_run = 0.f;        // sum of the rounded weights, this lane's half of the keys
 
     // ---- global -> register -> LDS staging of one K/V tile
     u32x4 reg_k[kChunks], reg_v[kChunks];
@@ -172,8 +256,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p)
 #pragma unroll
         for (int c = 0; c < kChunks; ++c) {
             const int chunk = tid + c * kThreads;
-            const int row = chunk / (D / 8);
-            const int col = (chunk % (D / 8)) * 8;
+            const int row = chunk / kUnits;
+            const int col = (chunk % kUnits) * 8;
             if (j0 + row < L) {
                 reg_k[c] = *reinterpret_cast<const u32x4 *>(kh + (int64_t)(j0 + row) * D + col);
                 reg_v[c] = *reinterpret_cast<const u32x4 *>(vh + (int64_t)(j0 + row) * D + col);
@@ -186,13 +270,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p)
     auto store_tile = [&](int buf) {
 #pragma unroll
         for (int c = 0; c < kChunks; ++c) {
-            const int chunk = tid + c * kThreads;
-            const int row = chunk / (D / 8);
-            const int col = (chunk % (D / 8)) * 8;
-            *reinterpret_cast<u32x4 *>(&lds_k[buf][row * KS + col]) = reg_k[c];
-            const T *vals = reinterpret_cast<const T *>(&reg_v[c]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) lds_v[buf][(col + e) * VS + row] = vals[e];
+            *reinterpret_cast<u32x4 *>(&lds[buf][0][st_k[c]]) = reg_k[c];
+            *reinterpret_cast<u32x4 *>(&lds[buf][1][st_v[c]]) = reg_v[c];
         }
     };
 
@@ -223,15 +302,14 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p)
             }
 
             // S^T for the two 32-key blocks of the tile
-            const T *tk = lds_k[buf];
+            const char *tk = lds[buf][0];
             f32x16 s[2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 s[kb] = f32x16{};
-                const T *krow = tk + (32 * kb + k_row_for_lane(l32)) * KS + 8 * hi;
 #pragma unroll
                 for (int ds = 0; ds < kDSteps; ++ds) {
-                    vec8 a = *reinterpret_cast<const vec8 *>(krow + 16 * ds);
+                    const vec8 a = *reinterpret_cast<const vec8 *>(tk + 32 * kb * kRowBytes + koff[ds]);
                     s[kb] = mfma32(a, qf[ds], s[kb]);
                 }
             }
@@ -247,41 +325,47 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p)
                     }
             }
 
-            // online softmax in the exp2 domain
+            // online softmax, exp2 domain; the reference max moves only when
+            // some row of the wave grew by more than kRescaleLog2
             float mt = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-            const float m_new = fmaxf(m_run, mt * p.scale_log2);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-            float psum = 0.f;
+            const float mt2 = half_swap_max(mt) * p.scale_log2;
+            if (__any(mt2 > m_run + kRescaleLog2)) {
+                const float m_new = fmaxf(m_run, mt2);
+                const float alpha = m_new > m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+                l_run *= alpha;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][r], p.scale_log2, -m_use));
-                    s[kb][r] = e;
-                    psum += e;
-                }
-            l_run = l_run * alpha + psum;
-            m_run = m_new;
-#pragma unroll
-            for (int i = 0; i < kDBlocks; ++i) acc_o[i] *= alpha;
+                for (int i = 0; i < kDBlocks; ++i) acc_o[i] *= alpha;
+                m_run = m_new;
+                neg_m = (m_new == -INFINITY) ? 0.f : -m_new;
+            }
 
             // O^T += V^T P^T over the four 16-key slices of the tile
-            const T *tv = lds_v[buf];
+            const char *tv = lds[buf][1];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 f32x8 pf;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) pf[e] = s[ks / 2][8 * (ks % 2) + e];
+                for (int e = 0; e < 8; ++e)
+                    pf[e] = __builtin_amdgcn_exp2f(fmaf(s[ks / 2][8 * (ks % 2) + e], p.scale_log2, neg_m));
                 const vec8 pv = __builtin_convertvector(pf, vec8);
+                if constexpr (std::is_same<T, _Float16>::value) {
+                    l_run = sum8(pv, l_run);  // the rounded weights, as the product uses them
+                } else {
+                    // bf16 rounding of the weights (2^-8) would reach the lse of short
+                    // rows, so the sum takes them in fp32
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) l_run += pf[e];
+                }
 #pragma unroll
                 for (int db = 0; db < kDBlocks; ++db) {
-                    vec8 a = *reinterpret_cast<const vec8 *>(tv + (32 * db + l32) * VS + 16 * ks + 8 * hi);
+                    const char *base = tv + 16 * ks * kRowBytes + voff[db];
+                    const s16x4 lo4 = lds_read_tr16(base);
+                    const s16x4 hi4 = lds_read_tr16(base + 4 * kRowBytes);
+                    const vec8 a = __builtin_bit_cast(vec8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
                     acc_o[db] = mfma32(a, pv, acc_o[db]);
                 }
             }
@@ -292,7 +376,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p)
 
     // ---- epilogue: one write of O and lse
     if (!wave_live || qi >= L) return;
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = half_swap_sum(l_run);
     const float inv = 1.f / l_tot;
     if (hi == 0) lseh[qi] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
     T *orow = oh + (int64_t)qi * D;

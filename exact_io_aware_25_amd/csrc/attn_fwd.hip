@@ -152,12 +152,10 @@ __device__ __forceinline__ float sum8(f16x8 v, float acc)
     return __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
 }
 
-// Rescale threshold of the online softmax, in log2 units: the reference
-// maximum of a row is only moved when a new score exceeds it by more than
-// this, so softmax weights stay <= 2^8 (well inside fp16 and fp32 range) and
-// the accumulator rescale is skipped on almost every tile.  The result is
-// the same exact softmax: any reference value cancels between O and the sum.
-constexpr float kRescaleLog2 = 8.0f;
+// Largest per-lane tile sum of softmax weights the fast path accepts.  It
+// bounds every weight by 2^15, inside fp16 range, and keeps the sum of a
+// whole row (at most 2^15 per key) far inside fp32 range.
+constexpr float kMaxTileSum = 32768.0f;
 
 template <typename T, int D, bool CAUSAL, bool WINDOW>
 __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p)
@@ -245,26 +243,31 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p)
     f32x16 acc_o[kDBlocks];
 #pragma unroll
     for (int i = 0; i < kDBlocks; ++i) acc_o[i] = f32x16{};
-    float m_run = -INFINITY;  // reference max of scale*log2(e)*s (log2 domain)
+    float m_run = -INFINITY;  // reference max of scale*log2(e)*s (log2 domain), -inf until a key is seen
     float neg_m = 0.f;        // -m_run, or 0 while m_run is -inf
     float l_run = 0.f;        // sum of the rounded weights, this lane's half of the keys
 
-    // ---- global -> register -> LDS staging of one K/V tile
+    // ---- global -> register -> LDS staging of one K/V tile.  Buffer loads
+    // through a resource that starts at the tile and ends at key L: rows past
+    // L read as zeros, which keeps every product finite (those keys are masked).
+    int ld_off[kChunks];
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+        const int chunk = tid + c * kThreads;
+        ld_off[c] = (chunk / kUnits) * kRowBytes + (chunk % kUnits) * 16;
+    }
     u32x4 reg_k[kChunks], reg_v[kChunks];
     auto load_tile = [&](int t) {
         const int j0 = t * kBlockK;
+        const int bytes = min(L - j0, kBlockK) * kRowBytes;  // keys j0 .. min(j0 + 63, L - 1)
+        const __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(kh + (int64_t)j0 * D), 0, bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(vh + (int64_t)j0 * D), 0, bytes, 0x00020000);
 #pragma unroll
         for (int c = 0; c < kChunks; ++c) {
-            const int chunk = tid + c * kThreads;
-            const int row = chunk / kUnits;
-            const int col = (chunk % kUnits) * 8;
-            if (j0 + row < L) {
-                reg_k[c] = *reinterpret_cast<const u32x4 *>(kh + (int64_t)(j0 + row) * D + col);
-                reg_v[c] = *reinterpret_cast<const u32x4 *>(vh + (int64_t)(j0 + row) * D + col);
-            } else {
-                reg_k[c] = u32x4{};  // keys past L: zeros keep the products finite
-                reg_v[c] = u32x4{};
-            }
+            reg_k[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ld_off[c], 0, 0));
+            reg_v[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, ld_off[c], 0, 0));
         }
     };
     auto store_tile = [&](int buf) {
@@ -325,48 +328,65 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p)
                     }
             }
 
-            // online softmax, exp2 domain; the reference max moves only when
-            // some row of the wave grew by more than kRescaleLog2
-            float mt = -INFINITY;
+            // Online softmax in the exp2 domain.  Fast path: weights against the
+            // current reference maximum, with no per-tile maximum.  If a weight
+            // of some row in the wave could exceed 2^15 (its tile sum does), or
+            // a row has no reference yet, the slow path takes the tile's true
+            // row maxima, moves the reference, rescales O and the sum, and
+            // recomputes the weights.  Either way the result is the exact
+            // softmax: the reference cancels between O and the sum.
+            vec8 pv[4];
+            float l_tile = 0.f;
+            auto weights = [&]() {
+                l_tile = 0.f;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+                for (int ks = 0; ks < 4; ++ks) {
+                    f32x8 pf;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-            const float mt2 = half_swap_max(mt) * p.scale_log2;
-            if (__any(mt2 > m_run + kRescaleLog2)) {
-                const float m_new = fmaxf(m_run, mt2);
-                const float alpha = m_new > m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-                l_run *= alpha;
+                    for (int e = 0; e < 8; ++e)
+                        pf[e] = __builtin_amdgcn_exp2f(fmaf(s[ks / 2][8 * (ks % 2) + e], p.scale_log2, neg_m));
+                    pv[ks] = __builtin_convertvector(pf, vec8);
+                    if constexpr (std::is_same<T, _Float16>::value) {
+                        l_tile = sum8(pv[ks], l_tile);  // the rounded weights, as the product uses them
+                    } else {
+                        // bf16 rounding of the weights (2^-8) would reach the lse of
+                        // short rows, so the sum takes them in fp32
 #pragma unroll
-                for (int i = 0; i < kDBlocks; ++i) acc_o[i] *= alpha;
-                m_run = m_new;
-                neg_m = (m_new == -INFINITY) ? 0.f : -m_new;
+                        for (int e = 0; e < 8; ++e) l_tile += pf[e];
+                    }
+                }
+            };
+            weights();
+            if (__any(!(l_tile <= kMaxTileSum) || m_run == -INFINITY)) {
+                float mt = -INFINITY;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+                const float m_new = fmaxf(m_run, half_swap_max(mt) * p.scale_log2);
+                if (__any(m_new > m_run)) {
+                    const float alpha = m_new > m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+                    l_run *= alpha;
+#pragma unroll
+                    for (int i = 0; i < kDBlocks; ++i) acc_o[i] *= alpha;
+                    m_run = m_new;
+                    neg_m = (m_new == -INFINITY) ? 0.f : -m_new;
+                    weights();
+                }
             }
+            l_run += l_tile;
 
             // O^T += V^T P^T over the four 16-key slices of the tile
             const char *tv = lds[buf][1];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                f32x8 pf;
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    pf[e] = __builtin_amdgcn_exp2f(fmaf(s[ks / 2][8 * (ks % 2) + e], p.scale_log2, neg_m));
-                const vec8 pv = __builtin_convertvector(pf, vec8);
-                if constexpr (std::is_same<T, _Float16>::value) {
-                    l_run = sum8(pv, l_run);  // the rounded weights, as the product uses them
-                } else {
-                    // bf16 rounding of the weights (2^-8) would reach the lse of short
-                    // rows, so the sum takes them in fp32
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) l_run += pf[e];
-                }
 #pragma unroll
                 for (int db = 0; db < kDBlocks; ++db) {
                     const char *base = tv + 16 * ks * kRowBytes + voff[db];
                     const s16x4 lo4 = lds_read_tr16(base);
                     const s16x4 hi4 = lds_read_tr16(base + 4 * kRowBytes);
                     const vec8 a = __builtin_bit_cast(vec8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-                    acc_o[db] = mfma32(a, pv, acc_o[db]);
+                    acc_o[db] = mfma32(a, pv[ks], acc_o[db]);
                 }
             }
         }

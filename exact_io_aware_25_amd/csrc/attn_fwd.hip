@@ -120,6 +120,14 @@ template <int D> __device__ __forceinline__ int v_swizzle(int row)
     return (c << 1) | (D == 128 ? ((c & 1) << 3) : 0);
 }
 
+// Copy 16 bytes per lane from a buffer into LDS without passing through
+// VGPRs: lane i's bytes land at lds_dst + 16*i (lds_dst is wave-uniform).
+__device__ __forceinline__ void copy_to_lds16(__amdgpu_buffer_rsrc_t src, void *lds_dst, int src_offset)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void *)lds_dst, 16,
+                                             src_offset, 0, 0, 0);
+}
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -168,8 +176,10 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p)
     constexpr int kDSteps = D / 16;                       // k-steps of the first product
     constexpr int kDBlocks = D / 32;                      // 32-row blocks of O^T
 
-    // [stage][K | V] tiles
-    __shared__ __attribute__((aligned(16))) char lds[2][2][kTileBytes];
+    // two stages of [K | V] tiles, as separate objects so the compiler can tell
+    // copies into one stage from reads of the other
+    __shared__ __attribute__((aligned(16))) char lds_a[2][kTileBytes];
+    __shared__ __attribute__((aligned(16))) char lds_b[2][kTileBytes];
 
     const int tid = threadIdx.x;
     const int wave = tid / 64;
@@ -231,15 +241,6 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p)
 #pragma unroll
     for (int db = 0; db < kDBlocks; ++db)
         voff[db] = tr_row * kRowBytes + 16 * ((4 * db + tr_unit) ^ v_swizzle<D>(tr_row)) + 8 * (lane & 1);
-    int st_k[kChunks], st_v[kChunks];
-#pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-        const int chunk = tid + c * kThreads;
-        const int row = chunk / kUnits, unit = chunk % kUnits;
-        st_k[c] = row * kRowBytes + 16 * (unit ^ k_swizzle<D>(row));
-        st_v[c] = row * kRowBytes + 16 * (unit ^ v_swizzle<D>(row));
-    }
-
     f32x16 acc_o[kDBlocks];
 #pragma unroll
     for (int i = 0; i < kDBlocks; ++i) acc_o[i] = f32x16{};
@@ -247,17 +248,22 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p)
     float neg_m = 0.f;        // -m_run, or 0 while m_run is -inf
     float l_run = 0.f;        // sum of the rounded weights, this lane's half of the keys
 
-    // ---- global -> register -> LDS staging of one K/V tile.  Buffer loads
-    // through a resource that starts at the tile and ends at key L: rows past
-    // L read as zeros, which keeps every product finite (those keys are masked).
-    int ld_off[kChunks];
+    // ---- global -> LDS copies of one K/V tile, straight into LDS (no VGPR
+    // staging).  A wave-wide copy instruction writes 64 consecutive 16-byte
+    // LDS units, one per lane in lane order, so lane i fetches the logical unit
+    // that the swizzle places at LDS unit i.  The buffer resource starts at the
+    // tile and ends at key L: rows past L read as zeros, keeping every product
+    // finite (those keys are masked).
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    int ld_k[kChunks], ld_v[kChunks];
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
-        const int chunk = tid + c * kThreads;
-        ld_off[c] = (chunk / kUnits) * kRowBytes + (chunk % kUnits) * 16;
+        const int unit_idx = (c * kWaves + wave) * 64 + lane;  // LDS unit this lane fills
+        const int row = unit_idx / kUnits, phys = unit_idx % kUnits;
+        ld_k[c] = row * kRowBytes + 16 * (phys ^ k_swizzle<D>(row));
+        ld_v[c] = row * kRowBytes + 16 * (phys ^ v_swizzle<D>(row));
     }
-    u32x4 reg_k[kChunks], reg_v[kChunks];
-    auto load_tile = [&](int t) {
+    auto copy_tile = [&](int t, char (*stage)[kTileBytes]) {
         const int j0 = t * kBlockK;
         const int bytes = min(L - j0, kBlockK) * kRowBytes;  // keys j0 .. min(j0 + 63, L - 1)
         const __amdgpu_buffer_rsrc_t rk =
@@ -266,27 +272,21 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p)
             __builtin_amdgcn_make_buffer_rsrc((void *)(vh + (int64_t)j0 * D), 0, bytes, 0x00020000);
 #pragma unroll
         for (int c = 0; c < kChunks; ++c) {
-            reg_k[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ld_off[c], 0, 0));
-            reg_v[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, ld_off[c], 0, 0));
-        }
-    };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-        for (int c = 0; c < kChunks; ++c) {
-            *reinterpret_cast<u32x4 *>(&lds[buf][0][st_k[c]]) = reg_k[c];
-            *reinterpret_cast<u32x4 *>(&lds[buf][1][st_v[c]]) = reg_v[c];
+            const int region = (c * kWaves + wave_u) * 1024;
+            copy_to_lds16(rk, &stage[0][region], ld_k[c]);
+            copy_to_lds16(rv, &stage[1][region], ld_v[c]);
         }
     };
 
-    if (t_begin < t_end) {
-        load_tile(t_begin);
-        store_tile(0);
-    }
+    if (t_begin < t_end) copy_tile(t_begin, lds_a);
 
-    for (int t = t_begin; t < t_end; ++t) {
-        const int buf = (t - t_begin) & 1;
-        if (t + 1 < t_end) load_tile(t + 1);
+    // One tile: wait for this wave's copies, barrier (the tile is then in LDS
+    // and every wave is done with the other stage), start copying the next
+    // tile into the other stage, then compute on this one.
+    auto process_tile = [&](int t, char (*cur)[kTileBytes], char (*nxt)[kTileBytes]) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
         __syncthreads();
+        if (t + 1 < t_end) copy_tile(t + 1, nxt);
 
         const int j0 = t * kBlockK;
         const int j_last = j0 + kBlockK - 1;
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p)
             }
 
             // S^T for the two 32-key blocks of the tile
-            const char *tk = lds[buf][0];
+            const char *tk = cur[0];
             f32x16 s[2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
@@ -377,7 +377,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p)
             l_run += l_tile;
 
             // O^T += V^T P^T over the four 16-key slices of the tile
-            const char *tv = lds[buf][1];
+            const char *tv = cur[1];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
@@ -390,8 +390,11 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p)
                 }
             }
         }
+    };
 
-        if (t + 1 < t_end) store_tile(buf ^ 1);
+    for (int t = t_begin; t < t_end; t += 2) {
+        process_tile(t, lds_a, lds_b);
+        if (t + 1 < t_end) process_tile(t + 1, lds_b, lds_a);
     }
 
     // ---- epilogue: one write of O and lse

@@ -45,11 +45,8 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = 32;
-constexpr int kBlockQ = kRowsPerWave * kWaves;  // query rows per workgroup
-constexpr int kBlockK = 64;                     // keys per K/V tile
+constexpr int kBlockK = 64;  // keys per K/V tile
 
 template <typename T> struct Vec8;
 template <> struct Vec8<_Float16> { typedef f16x8 type; };
@@ -165,10 +162,14 @@ __device__ __forceinline__ float sum8(f16x8 v, float acc)
 // whole row (at most 2^15 per key) far inside fp32 range.
 constexpr float kMaxTileSum = 32768.0f;
 
-template <typename T, int D, bool CAUSAL, bool WINDOW>
-__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p)
+// NW waves per workgroup, 32 query rows each; all of them share each K/V tile.
+template <typename T, int D, bool CAUSAL, bool WINDOW, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(Params p)
 {
     typedef typename Vec8<T>::type vec8;
+    constexpr int kWaves = NW;
+    constexpr int kThreads = 64 * NW;
+    constexpr int kBlockQ = kRowsPerWave * NW;  // query rows per workgroup
     constexpr int kRowBytes = 2 * D;                      // one K or V row in LDS
     constexpr int kTileBytes = kBlockK * kRowBytes;       // one K or V tile
     constexpr int kUnits = D / 8;                         // 16-byte units per row
@@ -307,6 +308,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p)
             // S^T for the two 32-key blocks of the tile
             const char *tk = cur[0];
             f32x16 s[2];
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 s[kb] = f32x16{};
@@ -317,6 +319,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p)
                 }
             }
 
+            __builtin_amdgcn_s_setprio(0);
             // mask: register r of block kb holds key j0 + 32*kb + 16*(r/8) + 8*hi + r%8
             if (!full) {
 #pragma unroll
@@ -336,9 +339,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p)
             // recomputes the weights.  Either way the result is the exact
             // softmax: the reference cancels between O and the sum.
             vec8 pv[4];
-            float l_tile = 0.f;
+            float l_tile = 0.f, part[4];
             auto weights = [&]() {
-                l_tile = 0.f;
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     f32x8 pf;
@@ -347,14 +349,16 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p)
                         pf[e] = __builtin_amdgcn_exp2f(fmaf(s[ks / 2][8 * (ks % 2) + e], p.scale_log2, neg_m));
                     pv[ks] = __builtin_convertvector(pf, vec8);
                     if constexpr (std::is_same<T, _Float16>::value) {
-                        l_tile = sum8(pv[ks], l_tile);  // the rounded weights, as the product uses them
+                        part[ks] = sum8(pv[ks], 0.f);  // the rounded weights, as the product uses them
                     } else {
                         // bf16 rounding of the weights (2^-8) would reach the lse of
                         // short rows, so the sum takes them in fp32
+                        part[ks] = 0.f;
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) l_tile += pf[e];
+                        for (int e = 0; e < 8; ++e) part[ks] += pf[e];
                     }
                 }
+                l_tile = (part[0] + part[1]) + (part[2] + part[3]);
             };
             weights();
             if (__any(!(l_tile <= kMaxTileSum) || m_run == -INFINITY)) {
@@ -378,6 +382,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p)
 
             // O^T += V^T P^T over the four 16-key slices of the tile
             const char *tv = cur[1];
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
@@ -389,6 +394,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_kernel(Params p)
                     acc_o[db] = mfma32(a, pv[ks], acc_o[db]);
                 }
             }
+            __builtin_amdgcn_s_setprio(0);
         }
     };
 
@@ -424,23 +430,37 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb)
     return na && nb && pa < pb + nb && pb < pa + na;
 }
 
-template <typename T, int D, bool CAUSAL, bool WINDOW>
-hipError_t launch_instance(const Params &p, dim3 grid, hipStream_t stream)
+// Workgroups of 8 waves needed before they are preferred over 4-wave ones:
+// a 256-row block halves the K/V traffic per FLOP, but below this the finer
+// 128-row grid keeps more of the 256 CUs busy.
+constexpr int64_t kWideMinBlocks = 512;
+
+template <typename T, int D, bool CAUSAL, bool WINDOW, int NW>
+hipError_t launch_waves(Params p, hipStream_t stream)
 {
-    Params args = p;
-    void *kargs[] = {&args};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&attn_fwd_kernel<T, D, CAUSAL, WINDOW>),
-                           grid, dim3(kThreads), kargs, 0, stream);
+    p.n_qblk = (p.L + kRowsPerWave * NW - 1) / (kRowsPerWave * NW);
+    const dim3 grid((unsigned)((int64_t)p.n_qblk * p.B * p.H));
+    void *kargs[] = {&p};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&attn_fwd_kernel<T, D, CAUSAL, WINDOW, NW>),
+                           grid, dim3(64 * NW), kargs, 0, stream);
+}
+
+template <typename T, int D, bool CAUSAL, bool WINDOW>
+hipError_t launch_instance(const Params &p, hipStream_t stream)
+{
+    const int64_t wide_blocks = (int64_t)((p.L + 255) / 256) * p.B * p.H;
+    return wide_blocks >= kWideMinBlocks ? launch_waves<T, D, CAUSAL, WINDOW, 8>(p, stream)
+                                         : launch_waves<T, D, CAUSAL, WINDOW, 4>(p, stream);
 }
 
 template <typename T, int D>
-hipError_t launch_mask(const Params &p, bool causal, bool window, dim3 grid, hipStream_t stream)
+hipError_t launch_mask(const Params &p, bool causal, bool window, hipStream_t stream)
 {
     if (causal)
-        return window ? launch_instance<T, D, true, true>(p, grid, stream)
-                      : launch_instance<T, D, true, false>(p, grid, stream);
-    return window ? launch_instance<T, D, false, true>(p, grid, stream)
-                  : launch_instance<T, D, false, false>(p, grid, stream);
+        return window ? launch_instance<T, D, true, true>(p, stream)
+                      : launch_instance<T, D, true, false>(p, stream);
+    return window ? launch_instance<T, D, false, true>(p, stream)
+                  : launch_instance<T, D, false, false>(p, stream);
 }
 
 template <typename T>
@@ -467,8 +487,7 @@ int attn_forward(const void *q, const void *k, const void *v, void *out, float *
     const size_t bytes_q = (size_t)(rows_q * d * sizeof(T));
     const size_t bytes_kv = (size_t)(rows_kv * d * sizeof(T));
     const size_t bytes_lse = (size_t)(rows_q * sizeof(float));
-    const int n_qblk = (L + kBlockQ - 1) / kBlockQ;
-    const int64_t blocks = (int64_t)n_qblk * B * H;
+    const int64_t blocks = (int64_t)((L + 127) / 128) * B * H;  // the finer of the two grids
     if (blocks > INT_MAX) return ATTN_ERR_SIZE;
     if (overlaps(out, bytes_q, q, bytes_q) || overlaps(out, bytes_q, k, bytes_kv) ||
         overlaps(out, bytes_q, v, bytes_kv) || overlaps(out, bytes_q, lse, bytes_lse) ||
@@ -488,14 +507,12 @@ int attn_forward(const void *q, const void *k, const void *v, void *out, float *
     p.L = L;
     p.group = H / H_kv;
     p.window = window;
-    p.n_qblk = n_qblk;
     p.scale_log2 = attn_resolve_scale(scale, d) * 1.4426950408889634f;
 
-    const dim3 grid((unsigned)blocks);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const bool win = window >= 0;
-    const hipError_t err = d == 64 ? launch_mask<T, 64>(p, causal, win, grid, s)
-                                   : launch_mask<T, 128>(p, causal, win, grid, s);
+    const hipError_t err = d == 64 ? launch_mask<T, 64>(p, causal, win, s)
+                                   : launch_mask<T, 128>(p, causal, win, s);
     return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 

@@ -64,13 +64,17 @@ def algorithmic_bytes(w) -> float:
 
 
 def time_workload(w, steps: int, warmup: int):
+    """Time `steps` calls after `warmup` calls, with HIP events recorded on the
+    stream the kernel is launched on.  Peak memory is taken as the pages do:
+    statistics reset after q, k, v exist, so it covers out, lse and anything
+    the call itself allocates (the library allocates nothing)."""
     dev = torch.device("cuda:0")
     q, k, v = (t.to(dev) for t in workload_inputs(w))
     torch.cuda.synchronize()
-    out = torch.empty_like(q)
-    lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev)
     torch.cuda.reset_peak_memory_stats(dev)
     base = torch.cuda.memory_allocated(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     for _ in range(warmup):
         attn.forward(q, k, v, causal=w.causal, window=w.window, scale=w.scale, out=out, lse=lse,
@@ -87,9 +91,9 @@ def time_workload(w, steps: int, warmup: int):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = start.elapsed_time(stop) / steps
-    peak_mem = torch.cuda.max_memory_allocated(dev)
-    return dict(ms=ms, wall_s=wall, out=out, lse=lse, inputs=(q, k, v), peak_mem=peak_mem,
-                extra_mem=peak_mem - base)
+    peak = torch.cuda.max_memory_allocated(dev)
+    return dict(ms=ms, wall_s=wall, out=out, lse=lse, inputs=(q, k, v),
+                peak_mem=peak, peak_mem_incl_inputs=peak, peak_mem_call=peak - base)
 
 
 def cpu_baseline(w, out, lse, inputs, budget_s: float = 15.0, seed: int = 7):
@@ -128,11 +132,49 @@ def cpu_baseline(w, out, lse, inputs, budget_s: float = 15.0, seed: int = 7):
                 parity_max_abs_o=err_o, parity_max_abs_lse=err_l)
 
 
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCE = os.path.join(ROOT, "exact_io_aware_25_amd", "csrc", "attn_fwd.hip")
+
+
+def kernel_source_sha256() -> str:
+    import hashlib
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+
+
+def profiled_traffic(w):
+    """Bytes per launch between L2 and memory for this workload, from the
+    committed rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE per
+    dispatch, each scaled by what the counter reads for a plain device copy
+    of known size); None when there is no summary for this workload or the
+    kernel source has changed since it was taken."""
+    path = os.path.join(PROFILES, f"attn_fwd_{w.name}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            key, val = line.split("=", 1)
+            vals[key.strip()] = val.strip()
+    if vals.get("workload") != w.name or vals.get("kernel_source_sha256") != kernel_source_sha256():
+        return None
+    copy_bytes = float(vals["copy_bytes"])
+    fetch_scale = copy_bytes / (float(vals["copy_fetch_kib"]) * 1024)
+    write_scale = copy_bytes / (float(vals["copy_write_kib"]) * 1024)
+    return (float(vals["fetch_kib_per_dispatch"]) * 1024 * fetch_scale
+            + float(vals["write_kib_per_dispatch"]) * 1024 * write_scale)
+
+
 def roofline_block(w, ms):
     flops = algorithmic_flops(w)
     achieved = flops / (ms * 1e-3) / 1e12
     return {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_PEAK_F16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_F16_TFLOPS, 4), "traffic": None}
+            "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_F16_TFLOPS, 4),
+            "traffic": profiled_traffic(w)}
+
+
+def loglog_slope(xs, ys):
+    lx, ly = np.log(np.asarray(xs, float)), np.log(np.asarray(ys, float))
+    return float(np.polyfit(lx, ly, 1)[0])
 
 
 def main():
@@ -185,7 +227,8 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.H_kv, "L": w.L, "d": w.d,
                    "causal": w.causal, "window": w.window, "scale": w.scale,
                    "algorithmic_flops": flops, "pct_of_mfma_peak": round(100 * tflops / MFMA_PEAK_F16_TFLOPS, 2),
-                   "peak_mem_bytes": r["peak_mem"], "algorithmic_bytes": algorithmic_bytes(w)},
+                   "peak_mem_bytes": r["peak_mem"], "peak_mem_call_bytes": r["peak_mem_call"],
+                   "algorithmic_bytes": algorithmic_bytes(w)},
         "roofline": roofline_block(w, r["ms"]),
     }
     if not args.no_cpu_baseline:
@@ -193,15 +236,30 @@ def main():
     print(json.dumps(line), flush=True)
 
     if args.sweep:
+        del r, line
+        torch.cuda.empty_cache()
+        sweep = []
         for name, ws in WORKLOADS.items():
             rs = time_workload(ws, max(5, args.steps), 3)
             f = algorithmic_flops(ws)
-            print(json.dumps({"workload": name, "ms": round(rs["ms"], 4),
-                              "tflops": round(f / (rs["ms"] * 1e-3) / 1e12, 2),
-                              "pct_peak": round(100 * f / (rs["ms"] * 1e-3) / 1e12 / MFMA_PEAK_F16_TFLOPS, 2),
-                              "peak_mem_bytes": rs["peak_mem"], "L": ws.L}), file=sys.stderr, flush=True)
+            rec = {"workload": name, "L": ws.L, "ms": round(rs["ms"], 4),
+                   "tflops": round(f / (rs["ms"] * 1e-3) / 1e12, 2),
+                   "pct_peak": round(100 * f / (rs["ms"] * 1e-3) / 1e12 / MFMA_PEAK_F16_TFLOPS, 2),
+                   "peak_mem_bytes": rs["peak_mem"], "peak_mem_call_bytes": rs["peak_mem_call"],
+                   "algorithmic_bytes": algorithmic_bytes(ws)}
+            sweep.append(rec)
+            print(json.dumps(rec), file=sys.stderr, flush=True)
             del rs
             torch.cuda.empty_cache()
+        # the pages' length sweep (causal, B=1, H=4, d=64): log-log slopes of time and memory
+        pts = sorted((rec["L"], rec["ms"], rec["peak_mem_bytes"]) for rec in sweep
+                     if rec["workload"] in ("causal_4k", "causal_8k", "causal_16k", "causal_32k",
+                                            "causal_64k", "causal_128k_h4"))
+        Ls, ts, ms_ = zip(*pts)
+        print(json.dumps({"length_sweep": {"L": Ls, "ms": ts, "peak_mem_bytes": ms_,
+                                           "slope_time": round(loglog_slope(Ls, ts), 3),
+                                           "slope_memory": round(loglog_slope(Ls, ms_), 3)}}),
+              file=sys.stderr, flush=True)
 
 
 if __name__ == "__main__":

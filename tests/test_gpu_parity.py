@@ -261,3 +261,28 @@ def test_errors_raise_before_launch():
     with pytest.raises(ValueError):
         attn.forward(q2[..., :64].contiguous(), k2[..., :64].contiguous(), v2[..., :64].contiguous(),
                      window=-3)
+
+
+# ------------------------------------------------------------------ both workgroup shapes
+# Grids of at least 512 blocks of 256 query rows run 8-wave workgroups (256
+# rows each); smaller grids run 4-wave workgroups (128 rows).  Many heads push
+# small, ragged shapes onto the 8-wave path; single heads of the same data go
+# through the 4-wave path, and the two must agree bitwise (each wave does the
+# same arithmetic on the same tiles in the same order).
+@pytest.mark.parametrize("dtype,d", [("f16", 64), ("bf16", 128)])
+@pytest.mark.parametrize("causal,window", [(True, -1), (False, -1), (True, 37), (False, 200)])
+def test_wide_and_narrow_workgroups_agree(dtype, d, causal, window):
+    L, H, H_kv = 300, 512, 128
+    announce(f"wide vs narrow: H={H}/{H_kv} L={L} d={d} {dtype} causal={causal} window={window}")
+    q, k, v = make_qkv(1, H, H_kv, L, d, dtype, 50 + d)
+    wide_o, wide_l = gpu_forward(q, k, v, causal, window, None)
+    group = H // H_kv
+    for g in (0, 57, 127):
+        hs = slice(g * group, (g + 1) * group)
+        o, l = gpu_forward(q[:, hs].contiguous(), k[:, g:g + 1].contiguous(), v[:, g:g + 1].contiguous(),
+                           causal, window, None)
+        assert torch.equal(o, wide_o[:, hs]) and torch.equal(l, wide_l[:, hs]), g
+    rows = [h * L + i for h in (0, 1, 255, 511) for i in (0, 1, 63, 64, 127, 128, 255, 256, 299)]
+    ref_o, ref_lse = oracle.attention(q, k, v, dtype, causal, window, 0.0, rows=rows)
+    check(wide_o.reshape(-1, d)[rows], wide_l.reshape(-1)[rows], ref_o, ref_lse, dtype,
+          f"wide {dtype} d={d}", vmax=float(v.abs().max()))

@@ -1,0 +1,259 @@
+// calibrate_gfx950.hip -- checks and measurements of the gfx950 features the
+// attention kernel relies on.  Not part of the library.
+//
+//   calibrate_gfx950 --check   verify lane layouts (exit status 0 = all hold):
+//       * ds_read_b64_tr_b16: within each 16-lane group, lane 4a+b receives
+//         element b of the 8-byte chunks addressed by lanes a, a+4, a+8, a+12;
+//       * v_permlane32_swap(x, x): first result = x of lane l%32, second =
+//         x of lane l%32 + 32;
+//       * buffer_load_dwordx4 ... lds: lane i's 16 bytes land at M0 + 16*i,
+//         read from lane i's own offset, and out-of-range lanes write zeros.
+//   calibrate_gfx950 --rates   issue rates per SIMD, no memory traffic:
+//       MFMA 32x32x16 f16 alone, the softmax VALU mix of one 64-key tile
+//       alone, both in one wave, and one MFMA wave beside one VALU wave.
+//
+// Every memory access stays inside the buffers it is given.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#define CHECK_HIP(x)                                                                  \
+    do {                                                                              \
+        hipError_t e_ = (x);                                                          \
+        if (e_ != hipSuccess) {                                                       \
+            std::printf("HIP error %s at line %d\n", hipGetErrorString(e_), __LINE__); \
+            return 2;                                                                 \
+        }                                                                             \
+    } while (0)
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+// ------------------------------------------------------------------ layout checks
+// One wave.  lds holds 1024 shorts; lane addresses stay below 2 KiB - 8 bytes.
+__global__ void tr16_layout(short *out)
+{
+    __shared__ short lds[1024];
+    const int lane = threadIdx.x;
+    for (int i = lane; i < 1024; i += 64) lds[i] = (short)i;
+    __syncthreads();
+    const int byte_addr = (lane % 16) * 64 + (lane / 16) * 8;  // 16 rows of 64 B, 4 column chunks
+    auto p = (__attribute__((address_space(3))) s16x4 *)((__attribute__((address_space(3))) char *)lds + byte_addr);
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
+    for (int e = 0; e < 4; ++e) out[lane * 4 + e] = v[e];
+}
+
+__global__ void swap_layout(int *out)
+{
+    const int lane = threadIdx.x;
+    const unsigned x = 1000 + lane;
+    auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    out[lane * 2] = r[0];
+    out[lane * 2 + 1] = r[1];
+}
+
+__device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t src, void *lds_dst, int off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void *)lds_dst, 16, off, 0, 0, 0);
+}
+
+// src: 64 chunks of 16 bytes; lane reads chunk (5*lane)%64; the resource
+// covers `records` bytes, so lanes whose chunk lies past it read zeros.
+__global__ void dma_layout(const unsigned *src, unsigned *out, int records)
+{
+    __shared__ __attribute__((aligned(16))) unsigned lds[1024];
+    const int lane = threadIdx.x;
+    for (int i = lane; i < 1024; i += 64) lds[i] = 0xdeadbeefu;
+    __syncthreads();
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void *)src, 0, records, 0x00020000);
+    copy16(r, lds + 256, ((5 * lane) % 64) * 16);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    for (int i = lane; i < 1024; i += 64) out[i] = lds[i];
+}
+
+static int run_checks()
+{
+    int failures = 0;
+    short *d_s;
+    int *d_i;
+    unsigned *d_src, *d_out;
+    CHECK_HIP(hipMalloc(&d_s, 256 * sizeof(short)));
+    CHECK_HIP(hipMalloc(&d_i, 128 * sizeof(int)));
+    CHECK_HIP(hipMalloc(&d_src, 256 * sizeof(unsigned)));
+    CHECK_HIP(hipMalloc(&d_out, 1024 * sizeof(unsigned)));
+
+    hipLaunchKernelGGL(tr16_layout, dim3(1), dim3(64), 0, 0, d_s);
+    CHECK_HIP(hipDeviceSynchronize());
+    std::vector<short> hs(256);
+    CHECK_HIP(hipMemcpy(hs.data(), d_s, 256 * sizeof(short), hipMemcpyDeviceToHost));
+    for (int lane = 0; lane < 64; ++lane) {
+        const int grp = lane / 16, a = (lane % 16) / 4, b = lane % 4;
+        for (int c = 0; c < 4; ++c) {
+            const int src_lane = 16 * grp + a + 4 * c;
+            const int want = (src_lane % 16) * 32 + (src_lane / 16) * 4 + b;  // element b of that lane's chunk
+            if (hs[lane * 4 + c] != want) ++failures;
+        }
+    }
+    std::printf("ds_read_b64_tr_b16 layout: %s\n", failures ? "MISMATCH" : "ok");
+
+    const int before_swap = failures;
+    hipLaunchKernelGGL(swap_layout, dim3(1), dim3(64), 0, 0, d_i);
+    CHECK_HIP(hipDeviceSynchronize());
+    std::vector<int> hi(128);
+    CHECK_HIP(hipMemcpy(hi.data(), d_i, 128 * sizeof(int), hipMemcpyDeviceToHost));
+    for (int lane = 0; lane < 64; ++lane)
+        if (hi[2 * lane] != 1000 + lane % 32 || hi[2 * lane + 1] != 1000 + lane % 32 + 32) ++failures;
+    std::printf("v_permlane32_swap layout: %s\n", failures > before_swap ? "MISMATCH" : "ok");
+
+    std::vector<unsigned> src(256);
+    for (int i = 0; i < 256; ++i) src[i] = i;
+    CHECK_HIP(hipMemcpy(d_src, src.data(), 256 * sizeof(unsigned), hipMemcpyHostToDevice));
+    std::vector<unsigned> ho(1024);
+    for (int records : {64 * 16, 32 * 16}) {
+        const int before = failures;
+        hipLaunchKernelGGL(dma_layout, dim3(1), dim3(64), 0, 0, d_src, d_out, records);
+        CHECK_HIP(hipDeviceSynchronize());
+        CHECK_HIP(hipMemcpy(ho.data(), d_out, 1024 * sizeof(unsigned), hipMemcpyDeviceToHost));
+        for (int i = 0; i < 1024; ++i) {
+            unsigned want = 0xdeadbeefu;
+            if (i >= 256 && i < 512) {
+                const int lane = (i - 256) / 4, word = (i - 256) % 4;
+                const int chunk = (5 * lane) % 64;
+                want = chunk * 16 < records ? (unsigned)(4 * chunk + word) : 0u;
+            }
+            if (ho[i] != want) ++failures;
+        }
+        std::printf("buffer_load ... lds placement (%d-byte range): %s\n", records,
+                    failures > before ? "MISMATCH" : "ok");
+    }
+    CHECK_HIP(hipFree(d_s));
+    CHECK_HIP(hipFree(d_i));
+    CHECK_HIP(hipFree(d_src));
+    CHECK_HIP(hipFree(d_out));
+    std::printf("%s\n", failures ? "CHECKS FAILED" : "all checks passed");
+    return failures ? 1 : 0;
+}
+
+// ------------------------------------------------------------------ issue rates
+// MODE 0: 16 MFMA per iteration (4 independent accumulators)
+// MODE 1: softmax VALU mix of one wave-tile (32 fma+exp2, 16 cvt, 16 dot2)
+// MODE 2: both, in every wave
+// MODE 3: even waves MFMA only, odd waves VALU only
+template <int MODE>
+__global__ void rates(float *out, int iters, long long *cycles)
+{
+    const int wave = threadIdx.x / 64;
+    f16x8 a, b;
+    for (int i = 0; i < 8; ++i) {
+        a[i] = (_Float16)(threadIdx.x * 1e-4f);
+        b[i] = (_Float16)1e-3f;
+    }
+    f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {}, s0, s1;
+    for (int i = 0; i < 16; ++i) {
+        s0[i] = threadIdx.x * 1e-3f + i;
+        s1[i] = -i * 1e-2f;
+    }
+    float acc = 0.f;
+    const bool do_mfma = MODE == 0 || MODE == 2 || (MODE == 3 && (wave & 1) == 0);
+    const bool do_valu = MODE == 1 || MODE == 2 || (MODE == 3 && (wave & 1) == 1);
+    const long long t0 = clock64();
+    for (int it = 0; it < iters; ++it) {
+        if (do_mfma) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c0, 0, 0, 0);
+                c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c1, 0, 0, 0);
+                c2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c2, 0, 0, 0);
+                c3 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c3, 0, 0, 0);
+            }
+        }
+        if (do_valu) {
+            float part[4];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                f32x8 pf;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    pf[e] = __builtin_amdgcn_exp2f(fmaf(ks < 2 ? s0[8 * (ks % 2) + e] : s1[8 * (ks % 2) + e], 0.18f, acc));
+                const f16x8 pv = __builtin_convertvector(pf, f16x8);
+                const f16x2 one = {1, 1};
+                float t = __builtin_amdgcn_fdot2(__builtin_shufflevector(pv, pv, 0, 1), one, 0.f, false);
+                t = __builtin_amdgcn_fdot2(__builtin_shufflevector(pv, pv, 2, 3), one, t, false);
+                t = __builtin_amdgcn_fdot2(__builtin_shufflevector(pv, pv, 4, 5), one, t, false);
+                part[ks] = __builtin_amdgcn_fdot2(__builtin_shufflevector(pv, pv, 6, 7), one, t, false);
+            }
+            acc = ((part[0] + part[1]) + (part[2] + part[3])) * 1e-12f;
+            s0[0] += acc;
+        }
+    }
+    const long long t1 = clock64();
+    float r = acc;
+    for (int i = 0; i < 16; ++i) r += c0[i] + c1[i] + c2[i] + c3[i] + s0[i] + s1[i];
+    out[blockIdx.x * blockDim.x + threadIdx.x] = r;
+    if (threadIdx.x == 0 && blockIdx.x == 0) cycles[0] = t1 - t0;
+}
+
+template <int MODE>
+static int time_mode(const char *name, int waves_per_simd, int cus, float *out, long long *cyc)
+{
+    const int threads = 256 * waves_per_simd, iters = 1000;
+    hipLaunchKernelGGL(rates<MODE>, dim3(cus), dim3(threads), 0, 0, out, iters, cyc);
+    hipEvent_t e0, e1;
+    CHECK_HIP(hipEventCreate(&e0));
+    CHECK_HIP(hipEventCreate(&e1));
+    CHECK_HIP(hipEventRecord(e0));
+    hipLaunchKernelGGL(rates<MODE>, dim3(cus), dim3(threads), 0, 0, out, iters, cyc);
+    CHECK_HIP(hipEventRecord(e1));
+    CHECK_HIP(hipEventSynchronize(e1));
+    float ms = 0;
+    CHECK_HIP(hipEventElapsedTime(&ms, e0, e1));
+    long long c = 0;
+    CHECK_HIP(hipMemcpy(&c, cyc, sizeof c, hipMemcpyDeviceToHost));
+    const double mfma_waves = MODE == 0 || MODE == 2 ? threads / 64.0 : (MODE == 3 ? threads / 128.0 : 0.0);
+    const double tflops = mfma_waves * 16 * 32768.0 * iters * cus / (ms * 1e-3) / 1e12;
+    std::printf("%-44s waves/SIMD %d  %8.3f ms  %7.1f clocks/iteration (wave 0)  MFMA %7.1f TFLOP/s\n", name,
+                waves_per_simd, ms, (double)c / iters, tflops);
+    CHECK_HIP(hipEventDestroy(e0));
+    CHECK_HIP(hipEventDestroy(e1));
+    return 0;
+}
+
+static int run_rates()
+{
+    hipDeviceProp_t prop;
+    CHECK_HIP(hipGetDeviceProperties(&prop, 0));
+    const int cus = prop.multiProcessorCount;
+    std::printf("device %s (%s), %d CUs, max clock %.2f GHz\n", prop.name, prop.gcnArchName, cus,
+                prop.clockRate * 1e-6);
+    float *out;
+    long long *cyc;
+    CHECK_HIP(hipMalloc(&out, (size_t)cus * 1024 * sizeof(float)));
+    CHECK_HIP(hipMalloc(&cyc, sizeof(long long)));
+    int rc = 0;
+    rc |= time_mode<0>("16 MFMA 32x32x16 f16", 1, cus, out, cyc);
+    rc |= time_mode<1>("softmax VALU mix of one 64-key tile", 1, cus, out, cyc);
+    rc |= time_mode<1>("softmax VALU mix of one 64-key tile", 4, cus, out, cyc);
+    rc |= time_mode<2>("both in every wave", 1, cus, out, cyc);
+    rc |= time_mode<2>("both in every wave", 2, cus, out, cyc);
+    rc |= time_mode<3>("MFMA-only wave beside VALU-only wave", 2, cus, out, cyc);
+    CHECK_HIP(hipFree(out));
+    CHECK_HIP(hipFree(cyc));
+    return rc;
+}
+
+int main(int argc, char **argv)
+{
+    const bool check = argc > 1 && std::strcmp(argv[1], "--check") == 0;
+    const bool rates_ = argc > 1 && std::strcmp(argv[1], "--rates") == 0;
+    if (!check && !rates_) {
+        std::printf("usage: %s --check | --rates\n", argv[0]);
+        return 2;
+    }
+    return check ? run_checks() : run_rates();
+}

@@ -309,13 +309,22 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(Params p)
             const char *tk = cur[0];
             f32x16 s[2];
             __builtin_amdgcn_s_setprio(1);
+            {
+                // every K fragment is read before the first product, so the LDS
+                // latency is paid once per tile instead of once per product (the
+                // registers are those of the previous tile's weights, dead here)
+                vec8 kf[2][kDSteps];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                s[kb] = f32x16{};
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int ds = 0; ds < kDSteps; ++ds) {
-                    const vec8 a = *reinterpret_cast<const vec8 *>(tk + 32 * kb * kRowBytes + koff[ds]);
-                    s[kb] = mfma32(a, qf[ds], s[kb]);
+                    for (int ds = 0; ds < kDSteps; ++ds)
+                        kf[kb][ds] = *reinterpret_cast<const vec8 *>(tk + 32 * kb * kRowBytes + koff[ds]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    s[kb] = f32x16{};
+#pragma unroll
+                    for (int ds = 0; ds < kDSteps; ++ds) s[kb] = mfma32(kf[kb][ds], qf[ds], s[kb]);
                 }
             }
 
@@ -383,15 +392,25 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(Params p)
             // O^T += V^T P^T over the four 16-key slices of the tile
             const char *tv = cur[1];
             __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
+            auto read_v = [&](int ks, vec8 (&vf)[kDBlocks]) {
 #pragma unroll
                 for (int db = 0; db < kDBlocks; ++db) {
                     const char *base = tv + 16 * ks * kRowBytes + voff[db];
                     const s16x4 lo4 = lds_read_tr16(base);
                     const s16x4 hi4 = lds_read_tr16(base + 4 * kRowBytes);
-                    const vec8 a = __builtin_bit_cast(vec8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-                    acc_o[db] = mfma32(a, pv[ks], acc_o[db]);
+                    vf[db] = __builtin_bit_cast(vec8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+                }
+            };
+            {
+                // the V fragments of slice ks+1 are read while slice ks multiplies
+                vec8 vf[2][kDBlocks];
+                read_v(0, vf[0]);
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    if (ks + 1 < 4) read_v(ks + 1, vf[(ks + 1) & 1]);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int db = 0; db < kDBlocks; ++db) acc_o[db] = mfma32(vf[ks & 1][db], pv[ks], acc_o[db]);
                 }
             }
             __builtin_amdgcn_s_setprio(0);

@@ -29,7 +29,7 @@ ATTN_ERR_FLAG = 8
 ATTN_ERR_SCALE = 9
 ATTN_ERR_ALIGN = 10
 
-EXPORTS = ("attn_fwd", "attn_fwd_bf16", "attn_status_string", "attn_resolve_scale")
+EXPORTS = ("attn_fwd", "attn_fwd_bf16", "attn_launch_shape", "attn_status_string", "attn_resolve_scale")
 
 _lib = None
 
@@ -61,6 +61,8 @@ def library():
         lib.attn_status_string.argtypes = [ctypes.c_int]
         lib.attn_resolve_scale.restype = ctypes.c_float
         lib.attn_resolve_scale.argtypes = [ctypes.c_float, ctypes.c_int]
+        lib.attn_launch_shape.restype = ctypes.c_int
+        lib.attn_launch_shape.argtypes = [ctypes.c_int] * 6 + [ctypes.POINTER(ctypes.c_int)] * 2
         _lib = lib
     return _lib
 
@@ -81,6 +83,15 @@ def attn_status_string(status: int) -> str:
 
 def attn_resolve_scale(scale: float, d: int) -> float:
     return float(library().attn_resolve_scale(float(scale), int(d)))
+
+
+def attn_launch_shape(B, H, L, d, causal, window):
+    """(waves per key-range group, key-range groups) attn_fwd would use; raises on bad arguments."""
+    waves, splits = ctypes.c_int(), ctypes.c_int()
+    st = library().attn_launch_shape(B, H, L, d, int(causal), window, ctypes.byref(waves), ctypes.byref(splits))
+    if st != ATTN_OK:
+        raise ValueError(attn_status_string(st))
+    return waves.value, splits.value
 
 
 def forward(q, k, v, causal: bool = False, window: int = -1, scale=None, out=None, lse=None,

@@ -162,13 +162,19 @@ __device__ __forceinline__ float sum8(f16x8 v, float acc)
 // whole row (at most 2^15 per key) far inside fp32 range.
 constexpr float kMaxTileSum = 32768.0f;
 
-// NW waves per workgroup, 32 query rows each; all of them share each K/V tile.
-template <typename T, int D, bool CAUSAL, bool WINDOW, int NW>
-__global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(Params p)
+// A workgroup owns NW*32 query rows of one (b, h).  Its waves form SPLIT
+// groups of NW waves; wave w of group s takes rows 32w.. of the block and the
+// s-th contiguous share of the block's key tiles.  The NW waves of a group
+// share each K/V tile of their share.  With SPLIT > 1 the groups' partial
+// results (O, reference max, sum) are merged at the end with the same exact
+// rescale the online softmax uses; this shortens the serial key loop of short
+// problems, whose grids are too small to fill the GPU.
+template <typename T, int D, bool CAUSAL, bool WINDOW, int NW, int SPLIT>
+__global__ __launch_bounds__(64 * NW * SPLIT) void attn_fwd_kernel(Params p)
 {
     typedef typename Vec8<T>::type vec8;
     constexpr int kWaves = NW;
-    constexpr int kThreads = 64 * NW;
+    constexpr int kThreads = 64 * NW;  // threads of one group
     constexpr int kBlockQ = kRowsPerWave * NW;  // query rows per workgroup
     constexpr int kRowBytes = 2 * D;                      // one K or V row in LDS
     constexpr int kTileBytes = kBlockK * kRowBytes;       // one K or V tile
@@ -177,13 +183,14 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(Params p)
     constexpr int kDSteps = D / 16;                       // k-steps of the first product
     constexpr int kDBlocks = D / 32;                      // 32-row blocks of O^T
 
-    // two stages of [K | V] tiles, as separate objects so the compiler can tell
-    // copies into one stage from reads of the other
-    __shared__ __attribute__((aligned(16))) char lds_a[2][kTileBytes];
-    __shared__ __attribute__((aligned(16))) char lds_b[2][kTileBytes];
+    // two stages of [group][K | V] tiles, as separate objects so the compiler
+    // can tell copies into one stage from reads of the other
+    __shared__ __attribute__((aligned(16))) char lds_a[SPLIT][2][kTileBytes];
+    __shared__ __attribute__((aligned(16))) char lds_b[SPLIT][2][kTileBytes];
 
     const int tid = threadIdx.x;
-    const int wave = tid / 64;
+    const int grp = SPLIT > 1 ? __builtin_amdgcn_readfirstlane(tid / 64 / NW) : 0;  // key-range group
+    const int wave = (tid / 64) % NW;                                // row block within the group
     const int lane = tid % 64;
     const int l32 = lane % 32;
     const int hi = lane / 32;
@@ -211,8 +218,12 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(Params p)
     if (WINDOW) kv_begin = max(0, q_first - p.window);
     if (CAUSAL) kv_end = q_last + 1;
     else if (WINDOW) kv_end = min(L, q_last + p.window + 1);
-    const int t_begin = kv_begin / kBlockK;
-    const int t_end = (kv_end + kBlockK - 1) / kBlockK;
+    const int t_first = kv_begin / kBlockK;
+    const int t_last = (kv_end + kBlockK - 1) / kBlockK;  // one past
+    const int chunk = SPLIT > 1 ? (t_last - t_first + SPLIT - 1) / SPLIT : t_last - t_first;
+    const int t_begin = SPLIT > 1 ? t_first + grp * chunk : t_first;  // this group's tiles
+    const int t_end = SPLIT > 1 ? min(t_last, t_begin + chunk) : t_last;
+    const int t_stop = SPLIT > 1 ? t_begin + chunk : t_last;          // steps every group runs
 
     // ---- this wave's query rows
     const int qa = q_first + wave * kRowsPerWave;
@@ -264,7 +275,7 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(Params p)
         ld_k[c] = row * kRowBytes + 16 * (phys ^ k_swizzle<D>(row));
         ld_v[c] = row * kRowBytes + 16 * (phys ^ v_swizzle<D>(row));
     }
-    auto copy_tile = [&](int t, char (*stage)[kTileBytes]) {
+    auto copy_tile = [&](int t, char (*stage)[2][kTileBytes]) {
         const int j0 = t * kBlockK;
         const int bytes = min(L - j0, kBlockK) * kRowBytes;  // keys j0 .. min(j0 + 63, L - 1)
         const __amdgpu_buffer_rsrc_t rk =
@@ -274,8 +285,8 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(Params p)
 #pragma unroll
         for (int c = 0; c < kChunks; ++c) {
             const int region = (c * kWaves + wave_u) * 1024;
-            copy_to_lds16(rk, &stage[0][region], ld_k[c]);
-            copy_to_lds16(rv, &stage[1][region], ld_v[c]);
+            copy_to_lds16(rk, &stage[grp][0][region], ld_k[c]);
+            copy_to_lds16(rv, &stage[grp][1][region], ld_v[c]);
         }
     };
 
@@ -284,14 +295,16 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(Params p)
     // One tile: wait for this wave's copies, barrier (the tile is then in LDS
     // and every wave is done with the other stage), start copying the next
     // tile into the other stage, then compute on this one.
-    auto process_tile = [&](int t, char (*cur)[kTileBytes], char (*nxt)[kTileBytes]) {
+    // (Every wave runs the same number of steps, `chunk`; a group whose share
+    // is shorter idles through the rest, still meeting every barrier.)
+    auto process_tile = [&](int t, char (*cur)[2][kTileBytes], char (*nxt)[2][kTileBytes]) {
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
         __syncthreads();
         if (t + 1 < t_end) copy_tile(t + 1, nxt);
 
         const int j0 = t * kBlockK;
         const int j_last = j0 + kBlockK - 1;
-        bool skip = !wave_live;
+        bool skip = !wave_live || (SPLIT > 1 && t >= t_end);
         if (CAUSAL) skip = skip || j0 > qb;
         if (WINDOW) {
             skip = skip || j_last < qa - p.window;
@@ -306,7 +319,7 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(Params p)
             }
 
             // S^T for the two 32-key blocks of the tile
-            const char *tk = cur[0];
+            const char *tk = cur[grp][0];
             f32x16 s[2];
             __builtin_amdgcn_s_setprio(1);
             {
@@ -390,7 +403,7 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(Params p)
             l_run += l_tile;
 
             // O^T += V^T P^T over the four 16-key slices of the tile
-            const char *tv = cur[1];
+            const char *tv = cur[grp][1];
             __builtin_amdgcn_s_setprio(1);
             auto read_v = [&](int ks, vec8 (&vf)[kDBlocks]) {
 #pragma unroll
@@ -417,13 +430,55 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_kernel(Params p)
         }
     };
 
-    for (int t = t_begin; t < t_end; t += 2) {
+    for (int t = t_begin; t < t_stop; t += 2) {
         process_tile(t, lds_a, lds_b);
-        if (t + 1 < t_end) process_tile(t + 1, lds_b, lds_a);
+        if (t + 1 < t_stop) process_tile(t + 1, lds_b, lds_a);
+    }
+
+    // ---- merge the groups' partial results into group 0, one group per
+    // round, through the now idle stage buffers: with M = max(m_0, m_s),
+    // O = 2^(m_0-M) O_0 + 2^(m_s-M) O_s and likewise the sums
+    if constexpr (SPLIT > 1) {
+        constexpr int kPart = 16 * kDBlocks + 2;  // floats per lane: O^T, reference max, sum
+        constexpr int kSlotBytes = 64 * kPart * 4;
+        constexpr int kPerBuffer = (int)sizeof(lds_a) / kSlotBytes;  // wave slots per stage buffer
+        constexpr int kBatch = 2 * kPerBuffer < NW ? 2 * kPerBuffer : NW;  // row blocks merged per round
+        static_assert(kPerBuffer >= 1, "merge slot does not fit");
+        for (int s = 1; s < SPLIT; ++s) {
+            for (int first = 0; first < NW; first += kBatch) {
+                const int i = wave - first;  // slot of this wave in the round
+                const bool in_round = i >= 0 && i < kBatch;
+                float *slot = reinterpret_cast<float *>(i < kPerBuffer ? &lds_a[0][0][0] : &lds_b[0][0][0]) +
+                              (i % kPerBuffer) * 64 * kPart;
+                __syncthreads();  // the previous round (or the last tile) is done with the buffers
+                if (grp == s && in_round) {
+#pragma unroll
+                    for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) slot[(16 * db + r) * 64 + lane] = acc_o[db][r];
+                    slot[(kPart - 2) * 64 + lane] = m_run;
+                    slot[(kPart - 1) * 64 + lane] = l_run;
+                }
+                __syncthreads();
+                if (grp == 0 && in_round) {
+                    const float m_s = slot[(kPart - 2) * 64 + lane];
+                    const float m_new = fmaxf(m_run, m_s);
+                    const float a_own = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+                    const float a_s = m_s == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_s - m_new);
+#pragma unroll
+                    for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            acc_o[db][r] = a_own * acc_o[db][r] + a_s * slot[(16 * db + r) * 64 + lane];
+                    l_run = a_own * l_run + a_s * slot[(kPart - 1) * 64 + lane];
+                    m_run = m_new;
+                }
+            }
+        }
     }
 
     // ---- epilogue: one write of O and lse
-    if (!wave_live || qi >= L) return;
+    if (grp != 0 || !wave_live || qi >= L) return;
     const float l_tot = half_swap_sum(l_run);
     const float inv = 1.f / l_tot;
     if (hi == 0) lseh[qi] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
@@ -449,27 +504,57 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb)
     return na && nb && pa < pb + nb && pb < pa + na;
 }
 
-// Workgroups of 8 waves needed before they are preferred over 4-wave ones:
-// a 256-row block halves the K/V traffic per FLOP, but below this the finer
-// 128-row grid keeps more of the 256 CUs busy.
-constexpr int64_t kWideMinBlocks = 512;
-
-template <typename T, int D, bool CAUSAL, bool WINDOW, int NW>
+template <typename T, int D, bool CAUSAL, bool WINDOW, int NW, int SPLIT>
 hipError_t launch_waves(Params p, hipStream_t stream)
 {
     p.n_qblk = (p.L + kRowsPerWave * NW - 1) / (kRowsPerWave * NW);
     const dim3 grid((unsigned)((int64_t)p.n_qblk * p.B * p.H));
     void *kargs[] = {&p};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&attn_fwd_kernel<T, D, CAUSAL, WINDOW, NW>),
-                           grid, dim3(64 * NW), kargs, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void *>(&attn_fwd_kernel<T, D, CAUSAL, WINDOW, NW, SPLIT>),
+                           grid, dim3(64 * NW * SPLIT), kargs, 0, stream);
+}
+
+// Workgroup shape: waves per key-range group (4 -> 128 query rows, 8 -> 256)
+// and number of key-range groups.  Measured on MI355X: 8-wave groups halve
+// K/V traffic per FLOP and win once the 256-row grid has >= 512 blocks; plain
+// causal grids have unequal blocks (the last one walks every key), so below
+// 2048 blocks their serial key loop is split (2 groups of 8 waves at d=64,
+// else 4 groups of 4 waves); other small grids split in 2.  Limits: a
+// 16-wave workgroup must fit 128 VGPRs per wave, which d=128 does not, and
+// four d=128 splits would not fit LDS.
+void launch_shape(int64_t B, int64_t H, int64_t L, int d, bool causal, int window, int *waves, int *splits)
+{
+    const int64_t g8 = (L + 255) / 256 * B * H;
+    const int64_t g4 = (L + 127) / 128 * B * H;
+    const bool unequal = causal && window < 0;
+    *waves = 8;
+    *splits = 1;
+    if (g8 >= 2048 || (g8 >= 512 && !unequal)) return;
+    if (g8 >= 512) {
+        *splits = d == 64 ? 2 : 1;
+        return;
+    }
+    *waves = 4;
+    if (unequal) *splits = d == 64 ? 4 : 2;
+    else *splits = g4 < 512 ? 2 : 1;
 }
 
 template <typename T, int D, bool CAUSAL, bool WINDOW>
 hipError_t launch_instance(const Params &p, hipStream_t stream)
 {
-    const int64_t wide_blocks = (int64_t)((p.L + 255) / 256) * p.B * p.H;
-    return wide_blocks >= kWideMinBlocks ? launch_waves<T, D, CAUSAL, WINDOW, 8>(p, stream)
-                                         : launch_waves<T, D, CAUSAL, WINDOW, 4>(p, stream);
+    int waves, splits;
+    launch_shape(p.B, p.H, p.L, D, CAUSAL, WINDOW ? p.window : -1, &waves, &splits);
+    if (waves == 8) {
+        if constexpr (D == 64) {
+            if (splits == 2) return launch_waves<T, D, CAUSAL, WINDOW, 8, 2>(p, stream);
+        }
+        return launch_waves<T, D, CAUSAL, WINDOW, 8, 1>(p, stream);
+    }
+    if constexpr (D == 64) {
+        if (splits == 4) return launch_waves<T, D, CAUSAL, WINDOW, 4, 4>(p, stream);
+    }
+    if (splits >= 2) return launch_waves<T, D, CAUSAL, WINDOW, 4, 2>(p, stream);
+    return launch_waves<T, D, CAUSAL, WINDOW, 4, 1>(p, stream);
 }
 
 template <typename T, int D>
@@ -555,6 +640,18 @@ int attn_fwd_bf16(const void *q, const void *k, const void *v, void *out, float 
                   int H_kv, int L, int d, int causal, int window, float scale, void *stream)
 {
     return attn_forward<__bf16>(q, k, v, out, lse, B, H, H_kv, L, d, causal, window, scale, stream);
+}
+
+int attn_launch_shape(int B, int H, int L, int d, int causal, int window, int *waves_per_group,
+                      int *key_splits)
+{
+    if (!waves_per_group || !key_splits) return ATTN_ERR_NULL;
+    if (B < 0 || L < 0 || H < 1) return ATTN_ERR_SHAPE;
+    if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+    if (window < -1) return ATTN_ERR_WINDOW;
+    if (causal != 0 && causal != 1) return ATTN_ERR_FLAG;
+    launch_shape(B, H, L, d, causal == 1, window, waves_per_group, key_splits);
+    return ATTN_OK;
 }
 
 const char *attn_status_string(int status)

@@ -93,6 +93,15 @@ int attn_fwd_bf16(const void *q, const void *k, const void *v, void *out, float 
 /* A static, human-readable name for a status code (never NULL). */
 const char *attn_status_string(int status);
 
+/* How attn_fwd / attn_fwd_bf16 would launch a problem of this shape: each
+ * workgroup takes 32 * (*waves_per_group) query rows of one (batch, head),
+ * and its waves form *key_splits groups that each walk a contiguous share of
+ * the keys (their partial softmax results are merged exactly at the end).
+ * Host-only; makes no HIP call.  Returns an attn_status (argument checks as
+ * for attn_fwd; H_kv plays no part). */
+int attn_launch_shape(int B, int H, int L, int d, int causal, int window, int *waves_per_group,
+                      int *key_splits);
+
 /* The fp32 scale the kernels use for a given scale argument and head size:
  * `scale` itself when finite and > 0, else the fp32 value nearest 1/sqrt(d).
  * Host-only; makes no HIP call. */

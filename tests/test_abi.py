@@ -92,3 +92,28 @@ def test_binding_does_not_import_the_oracle():
     assert "oracle" not in src.replace("no fallback", "")
     hip = open(os.path.join(ROOT, "exact_io_aware_25_amd", "csrc", "attn_fwd.hip")).read()
     assert "oracle" not in hip
+
+
+def test_launch_shape():
+    """Problem shape -> (waves per key-range group, key-range groups)."""
+    shape = attn.attn_launch_shape
+    assert shape(1, 4, 131072, 64, True, -1) == (8, 1)      # long causal: 2048 blocks of 256 rows
+    assert shape(1, 4, 32768, 64, True, -1) == (8, 2)       # mid causal: split the key loop in 2
+    assert shape(1, 4, 32768, 128, True, -1) == (8, 1)      # d=128 cannot run 16-wave groups
+    assert shape(1, 4, 4096, 64, True, -1) == (4, 4)        # short causal: 4 key splits
+    assert shape(1, 4, 4096, 128, True, -1) == (4, 2)
+    assert shape(2, 8, 2048, 64, False, -1) == (4, 2)       # short non-causal
+    assert shape(1, 32, 16384, 128, True, 4096) == (8, 1)   # windowed: blocks of equal work
+    assert shape(1, 300, 200, 64, False, -1) == (4, 1)
+    for d in (64, 128):
+        for causal in (0, 1):
+            for window in (-1, 0, 100):
+                for B, H, L in ((1, 1, 1), (2, 8, 300), (1, 64, 65536), (3, 5, 777)):
+                    waves, splits = shape(B, H, L, d, causal, window)
+                    assert waves in (4, 8) and splits in (1, 2, 4)
+                    assert not (d == 128 and splits == 4) and not (waves == 8 and splits == 4)
+                    assert not (waves == 8 and splits == 2 and d == 128)
+    with pytest.raises(ValueError):
+        shape(1, 4, 100, 96, True, -1)
+    with pytest.raises(ValueError):
+        shape(1, 4, 100, 64, 2, -1)

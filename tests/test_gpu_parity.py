@@ -263,26 +263,43 @@ def test_errors_raise_before_launch():
                      window=-3)
 
 
-# ------------------------------------------------------------------ both workgroup shapes
-# Grids of at least 512 blocks of 256 query rows run 8-wave workgroups (256
-# rows each); smaller grids run 4-wave workgroups (128 rows).  Many heads push
-# small, ragged shapes onto the 8-wave path; single heads of the same data go
-# through the 4-wave path, and the two must agree bitwise (each wave does the
-# same arithmetic on the same tiles in the same order).
-@pytest.mark.parametrize("dtype,d", [("f16", 64), ("bf16", 128)])
-@pytest.mark.parametrize("causal,window", [(True, -1), (False, -1), (True, 37), (False, 200)])
-def test_wide_and_narrow_workgroups_agree(dtype, d, causal, window):
-    L, H, H_kv = 300, 512, 128
-    announce(f"wide vs narrow: H={H}/{H_kv} L={L} d={d} {dtype} causal={causal} window={window}")
-    q, k, v = make_qkv(1, H, H_kv, L, d, dtype, 50 + d)
-    wide_o, wide_l = gpu_forward(q, k, v, causal, window, None)
-    group = H // H_kv
-    for g in (0, 57, 127):
-        hs = slice(g * group, (g + 1) * group)
-        o, l = gpu_forward(q[:, hs].contiguous(), k[:, g:g + 1].contiguous(), v[:, g:g + 1].contiguous(),
-                           causal, window, None)
-        assert torch.equal(o, wide_o[:, hs]) and torch.equal(l, wide_l[:, hs]), g
-    rows = [h * L + i for h in (0, 1, 255, 511) for i in (0, 1, 63, 64, 127, 128, 255, 256, 299)]
+# ------------------------------------------------------------------ every launch shape
+# The library picks, per problem, 4- or 8-wave key-range groups (128 or 256
+# query rows per workgroup) and 1, 2 or 4 key-range groups merged at the end.
+# Each case below is a shape that attn_launch_shape confirms takes a given
+# path; sampled rows (first and last of heads, tile, block and split
+# boundaries, the ragged tail) are checked against the oracle.
+SHAPE_CASES = [
+    # (waves, splits, d, dtype, causal, window, B, H, H_kv, L)
+    (4, 4, 64, "f16", True, -1, 1, 4, 2, 300),
+    (4, 2, 128, "bf16", True, -1, 1, 4, 1, 300),
+    (4, 2, 64, "bf16", False, -1, 2, 4, 4, 333),
+    (4, 2, 128, "f16", True, 37, 1, 8, 2, 300),
+    (4, 1, 64, "f16", False, 50, 1, 300, 100, 200),
+    (4, 1, 128, "bf16", False, -1, 1, 300, 300, 200),
+    (8, 1, 64, "bf16", False, -1, 1, 512, 128, 300),
+    (8, 1, 128, "f16", True, -1, 1, 512, 64, 300),
+    (8, 1, 64, "f16", True, -1, 1, 1024, 256, 300),
+    (8, 1, 64, "f16", True, 100, 1, 512, 512, 300),
+    (8, 2, 64, "f16", True, -1, 1, 512, 128, 300),
+    (8, 2, 64, "bf16", True, -1, 2, 256, 256, 520),
+]
+
+
+def sample_rows_for(B, H, L, heads):
+    rows_in_head = sorted({0, 1, 31, 32, 63, 64, 127, 128, 129, 191, 255, 256, 257, 383, 384, 511, 512,
+                           L // 2, L // 3, L - 2, L - 1} & set(range(L)))
+    return [(b * H + h) * L + i for b in range(B) for h in heads for i in rows_in_head]
+
+
+@pytest.mark.parametrize("case", SHAPE_CASES, ids=lambda c: f"w{c[0]}s{c[1]}-d{c[2]}-{c[3]}-c{int(c[4])}w{c[5]}")
+def test_every_launch_shape(case):
+    waves, splits, d, dtype, causal, window, B, H, H_kv, L = case
+    assert attn.attn_launch_shape(B, H, L, d, causal, window) == (waves, splits)
+    announce(f"launch shape {waves}x{splits}: B={B} H={H}/{H_kv} L={L} d={d} {dtype} causal={causal} window={window}")
+    q, k, v = make_qkv(B, H, H_kv, L, d, dtype, 70 + waves * 10 + splits + d)
+    out, lse = gpu_forward(q, k, v, causal, window, None)
+    rows = sample_rows_for(B, H, L, sorted({0, 1, H // 2, H - 1}))
     ref_o, ref_lse = oracle.attention(q, k, v, dtype, causal, window, 0.0, rows=rows)
-    check(wide_o.reshape(-1, d)[rows], wide_l.reshape(-1)[rows], ref_o, ref_lse, dtype,
-          f"wide {dtype} d={d}", vmax=float(v.abs().max()))
+    check(out.reshape(-1, d)[rows], lse.reshape(-1)[rows], ref_o, ref_lse, dtype,
+          f"shape {waves}x{splits}", vmax=float(v.abs().max()))

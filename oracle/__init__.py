@@ -12,6 +12,10 @@ Two independent implementations of the same plain definition live here:
 * ``brute.py``: whole-matrix NumPy fp64 attention with an explicit boolean
   mask, used only to check the C oracle on tiny inputs.
 
+``attn_oracle.c`` also holds the backward pass (``attention_bwd``): the
+gradients of the same definition with respect to q, k and v for an upstream
+gradient dO, in fp64.
+
 The definition both follow is softmax(scale * Q K^T + mask) V with the
 natural-log logsumexp of each row («Оптимизация внимания Flash», Workflow 1,
 Steps 2 and 4; Workflow 2, Steps 2-3; «Что такое memory-efficient attention
@@ -61,6 +65,12 @@ def _bind(lib):
                                 ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                 ctypes.c_int, ctypes.c_int, ctypes.c_float,
                                 i64p, ctypes.c_int64, f64p, f64p, ctypes.c_int]
+    lib.oracle_attn_bwd.restype = ctypes.c_int
+    lib.oracle_attn_bwd.argtypes = [u16p, u16p, u16p, u16p, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                    i64p, ctypes.c_int64, i64p, ctypes.c_int64,
+                                    f64p, f64p, f64p, ctypes.c_int]
     lib.oracle_decode.restype = None
     lib.oracle_decode.argtypes = [u16p, f64p, ctypes.c_int64, ctypes.c_int]
     lib.oracle_resolve_scale.restype = ctypes.c_float
@@ -152,3 +162,48 @@ def attention(q, k, v, dtype: str, causal: bool, window: int = -1, scale: float 
     if rows is None:
         return out.reshape(B, H, L, d), lse.reshape(B, H, L)
     return out, lse
+
+
+def _row_ids(rows, total):
+    if rows is None:
+        return None, total, None
+    arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    if arr.size and (arr.min() < 0 or arr.max() >= total):
+        raise ValueError("row id out of range")
+    return arr, arr.size, _ptr(arr, ctypes.c_int64)
+
+
+def attention_bwd(q, k, v, dout, dtype: str, causal: bool, window: int = -1, scale: float = 0.0,
+                  q_rows=None, kv_rows=None, threads: int = 0, lib=None):
+    """Gradients of exact attention of 16-bit inputs, in fp64.
+
+    q, dout: [B,H,L,d]; k, v: [B,H_kv,L,d] (torch tensors or uint16 arrays of
+    bit patterns).  ``q_rows``: optional flat ids (b*H + h)*L + i of the dq
+    rows wanted; ``kv_rows``: optional flat ids (b*H_kv + g)*L + j of the
+    dk/dv rows wanted (an empty list skips that part).
+    Returns (dq, dk, dv): fp64 [B,H,L,d], [B,H_kv,L,d], [B,H_kv,L,d], or
+    [n_q, d], [n_kv, d], [n_kv, d] for the requested rows.
+    """
+    lib = lib or _default_lib()
+    qb, kb, vb, gb = _bits(q), _bits(k), _bits(v), _bits(dout)
+    B, H, L, d = qb.shape
+    H_kv = kb.shape[1]
+    if kb.shape != (B, H_kv, L, d) or vb.shape != kb.shape or gb.shape != qb.shape:
+        raise ValueError(f"shape mismatch q{qb.shape} k{kb.shape} v{vb.shape} dout{gb.shape}")
+    qa, nq, qp = _row_ids(q_rows, B * H * L)
+    ka, nk, kp = _row_ids(kv_rows, B * H_kv * L)
+    dq = np.zeros((nq, d), np.float64)
+    dk = np.zeros((nk, d), np.float64)
+    dv = np.zeros((nk, d), np.float64)
+    st = lib.oracle_attn_bwd(_ptr(qb, ctypes.c_uint16), _ptr(kb, ctypes.c_uint16), _ptr(vb, ctypes.c_uint16),
+                             _ptr(gb, ctypes.c_uint16), DTYPES[dtype], B, H, H_kv, L, d,
+                             int(bool(causal)), int(window), float(scale), qp, nq, kp, nk,
+                             _ptr(dq, ctypes.c_double), _ptr(dk, ctypes.c_double),
+                             _ptr(dv, ctypes.c_double), int(threads))
+    if st != 0:
+        raise ValueError(f"oracle_attn_bwd failed with status {st}")
+    if q_rows is None:
+        dq = dq.reshape(B, H, L, d)
+    if kv_rows is None:
+        dk, dv = dk.reshape(B, H_kv, L, d), dv.reshape(B, H_kv, L, d)
+    return dq, dk, dv

@@ -126,6 +126,53 @@ static int reads_kv_head(int64_t r, int b, int g, int H, int H_kv, int L)
     return bh / H == b && oracle_kv_head((int)(bh % H), H, H_kv) == g;
 }
 
+/* One query row i of the definition: its scores s_ij of the visible keys,
+ * their maximum m, l = sum_j exp(s_ij - m), and acc = sum_j exp(s_ij - m) v_j
+ * (so O_i = acc / l).  qd: the row's decoded q; kd, vd: the decoded K/V head.
+ * If dod (the row's decoded upstream gradient) is not NULL, also
+ * D = dO_i . O_i for the backward pass.  Returns 0, or -2 if the row sees no
+ * key. */
+static int row_softmax(const double *qd, const double *dod, const double *kd, const double *vd,
+                       int64_t i, int L, int d, int causal, int window, double sc,
+                       double *s, double *acc, double *m_out, double *l_out, double *D_out)
+{
+    double m = -INFINITY;
+    int64_t count = 0;
+    for (int64_t j = 0; j < L; ++j) {
+        if (!oracle_visible(i, j, causal, window))
+            continue;
+        double dot = 0.0;
+        for (int c = 0; c < d; ++c)
+            dot += qd[c] * kd[j * d + c];
+        s[j] = sc * dot;
+        if (s[j] > m)
+            m = s[j];
+        ++count;
+    }
+    if (count == 0)
+        return -2;
+    double l = 0.0;
+    for (int c = 0; c < d; ++c)
+        acc[c] = 0.0;
+    for (int64_t j = 0; j < L; ++j) {
+        if (!oracle_visible(i, j, causal, window))
+            continue;
+        double p = exp(s[j] - m);
+        l += p;
+        for (int c = 0; c < d; ++c)
+            acc[c] += p * vd[j * d + c];
+    }
+    *m_out = m;
+    *l_out = l;
+    if (dod) {
+        double D = 0.0;
+        for (int c = 0; c < d; ++c)
+            D += dod[c] * (acc[c] / l);
+        *D_out = D;
+    }
+    return 0;
+}
+
 /*
  * Exact attention for a set of query rows.
  *
@@ -187,37 +234,12 @@ int oracle_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v, int dty
                     int64_t i = r % L;
                     oracle_decode(q + r * d, qd, d, dtype);
 
-                    /* scores of the visible keys, and their maximum */
-                    double m = -INFINITY;
-                    int64_t count = 0;
-                    for (int64_t j = 0; j < L; ++j) {
-                        if (!oracle_visible(i, j, causal, window))
-                            continue;
-                        double dot = 0.0;
-                        for (int c = 0; c < d; ++c)
-                            dot += qd[c] * kd[j * d + c];
-                        s[j] = sc * dot;
-                        if (s[j] > m)
-                            m = s[j];
-                        ++count;
-                    }
-                    if (count == 0) {
+                    double m, l;
+                    if (row_softmax(qd, NULL, kd, vd, i, L, d, causal, window, sc, s, acc, &m, &l,
+                                    NULL) != 0) {
 #pragma omp atomic write
                         status = -2;
                         continue;
-                    }
-
-                    /* softmax weights, their sum, and the weighted sum of values */
-                    double l = 0.0;
-                    for (int c = 0; c < d; ++c)
-                        acc[c] = 0.0;
-                    for (int64_t j = 0; j < L; ++j) {
-                        if (!oracle_visible(i, j, causal, window))
-                            continue;
-                        double p = exp(s[j] - m);
-                        l += p;
-                        for (int c = 0; c < d; ++c)
-                            acc[c] += p * vd[j * d + c];
                     }
                     for (int c = 0; c < d; ++c)
                         out[t * d + c] = acc[c] / l;
@@ -231,5 +253,215 @@ int oracle_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v, int dty
     }
     free(kd);
     free(vd);
+    return status;
+}
+
+/*
+ * Gradients of exact attention: the backward pass.
+ *
+ * The pages recommend FlashAttention for training as well as inference
+ * («Оптимизация внимания Flash», introduction) and list the backward pass as
+ * unmeasured in their benchmark («ТЕХНИЧЕСКОЕ ЗАДАНИЕ: Сравнить Hyena vs
+ * FlashAttention на 128k», stage 5); they give no formula for it.  The
+ * backward pass is therefore the gradient of the forward definition above:
+ * for an upstream gradient dO of the output, with P_ij = exp(s_ij - m_i) / l_i
+ * the softmax weight of a visible pair,
+ *
+ *   dv_j  = sum over query heads h reading g, and rows i that see j, of P_ij dO_i
+ *   dP_ij = dO_i . v_j
+ *   D_i   = dO_i . O_i                 (= sum_j P_ij dP_ij)
+ *   dS_ij = P_ij (dP_ij - D_i)         (the softmax Jacobian applied to dP)
+ *   dq_i  = scale * sum_j dS_ij k_j
+ *   dk_j  = scale * sum over the same (h, i) of dS_ij q_i
+ *
+ * A K/V head receives the gradients of every query head that reads it.
+ * Everything is fp64 from the exactly decoded 16-bit inputs; nothing is tiled
+ * or reordered beyond recomputing a row's statistics where they are needed.
+ */
+
+/*
+ * q, dout: [B,H,L,d]; k, v: [B,H_kv,L,d]; 16-bit patterns of `dtype`.
+ * q_rows: flat ids (b*H + h)*L + i of the dq rows wanted, or NULL for all
+ *   (then n_q_rows is ignored); dq: [n_q_rows, d].
+ * kv_rows: flat ids (b*H_kv + g)*L + j of the dk/dv rows wanted, or NULL for
+ *   all; dk, dv: [n_kv_rows, d].
+ * Returns 0, -1 for bad arguments or no memory, -2 if a row has no visible key.
+ */
+int oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
+                    int dtype, int B, int H, int H_kv, int L, int d, int causal, int window,
+                    float scale, const int64_t *q_rows, int64_t n_q_rows, const int64_t *kv_rows,
+                    int64_t n_kv_rows, double *dq, double *dk, double *dv, int threads)
+{
+    if (B < 0 || H <= 0 || H_kv <= 0 || L < 0 || d <= 0 || H % H_kv != 0 || window < -1)
+        return -1;
+    if (q_rows == NULL)
+        n_q_rows = (int64_t)B * H * L;
+    if (kv_rows == NULL)
+        n_kv_rows = (int64_t)B * H_kv * L;
+    if (n_q_rows == 0 && n_kv_rows == 0)
+        return 0;
+    const double sc = (double)oracle_resolve_scale(scale, d);
+    const int group = H / H_kv;
+    const int64_t head_elems = (int64_t)L * d;
+    const int64_t group_rows = (int64_t)group * L;
+    if (threads <= 0)
+        threads = omp_get_max_threads();
+
+    double *kd = malloc(sizeof(double) * (size_t)head_elems);
+    double *vd = malloc(sizeof(double) * (size_t)head_elems);
+    double *qd = malloc(sizeof(double) * (size_t)(group_rows * d));
+    double *dod = malloc(sizeof(double) * (size_t)(group_rows * d));
+    double *m = malloc(sizeof(double) * (size_t)group_rows);
+    double *l = malloc(sizeof(double) * (size_t)group_rows);
+    double *Dr = malloc(sizeof(double) * (size_t)group_rows);
+    char *needed = malloc((size_t)group_rows);
+    int status = 0;
+    if (!kd || !vd || !qd || !dod || !m || !l || !Dr || !needed)
+        status = -1;
+
+    for (int b = 0; b < B && status == 0; ++b) {
+        for (int g = 0; g < H_kv && status == 0; ++g) {
+            const int h0 = g * group;  /* first query head reading g */
+            const int64_t kv_base = ((int64_t)b * H_kv + g) * L;
+
+            /* which rows of this (b, g) are wanted */
+            int any = 0;
+            memset(needed, 0, (size_t)group_rows);
+            for (int64_t t = 0; t < n_q_rows; ++t) {
+                int64_t r = q_rows ? q_rows[t] : t;
+                int64_t bh = r / L;
+                if (bh / H == b && oracle_kv_head((int)(bh % H), H, H_kv) == g) {
+                    needed[(bh % H - h0) * L + r % L] = 1;
+                    any = 1;
+                }
+            }
+            /* every row that sees a wanted key needs its statistics too */
+            for (int64_t t = 0; t < n_kv_rows; ++t) {
+                int64_t r = kv_rows ? kv_rows[t] : t;
+                if (r / L != (int64_t)b * H_kv + g)
+                    continue;
+                any = 1;
+                int64_t j = r % L;
+                for (int hh = 0; hh < group; ++hh)
+                    for (int64_t i = 0; i < L; ++i)
+                        if (oracle_visible(i, j, causal, window))
+                            needed[hh * L + i] = 1;
+            }
+            if (!any)
+                continue;
+
+            oracle_decode(k + kv_base * d, kd, head_elems, dtype);
+            oracle_decode(v + kv_base * d, vd, head_elems, dtype);
+            const int64_t q_base = ((int64_t)b * H + h0) * L;
+            oracle_decode(q + q_base * d, qd, group_rows * d, dtype);
+            oracle_decode(dout + q_base * d, dod, group_rows * d, dtype);
+
+            /* 1. row statistics */
+#pragma omp parallel num_threads(threads)
+            {
+                double *s = malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+                double *acc = malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(dynamic, 8)
+                for (int64_t r = 0; r < group_rows; ++r) {
+                    if (!needed[r])
+                        continue;
+                    if (row_softmax(qd + r * d, dod + r * d, kd, vd, r % L, L, d, causal, window, sc,
+                                  s, acc, &m[r], &l[r], &Dr[r]) != 0) {
+#pragma omp atomic write
+                        status = -2;
+                    }
+                }
+                free(s);
+                free(acc);
+            }
+            if (status != 0)
+                break;
+
+            /* 2. dq_i = scale * sum_j dS_ij k_j */
+#pragma omp parallel num_threads(threads)
+            {
+                double *acc = malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(dynamic, 8)
+                for (int64_t t = 0; t < n_q_rows; ++t) {
+                    int64_t r = q_rows ? q_rows[t] : t;
+                    int64_t bh = r / L;
+                    if (bh / H != b || oracle_kv_head((int)(bh % H), H, H_kv) != g)
+                        continue;
+                    const int64_t gr = (bh % H - h0) * L + r % L;  /* row within the group */
+                    const int64_t i = r % L;
+                    const double *qi = qd + gr * d, *doi = dod + gr * d;
+                    for (int c = 0; c < d; ++c)
+                        acc[c] = 0.0;
+                    for (int64_t j = 0; j < L; ++j) {
+                        if (!oracle_visible(i, j, causal, window))
+                            continue;
+                        double dot = 0.0, dP = 0.0;
+                        for (int c = 0; c < d; ++c) {
+                            dot += qi[c] * kd[j * d + c];
+                            dP += doi[c] * vd[j * d + c];
+                        }
+                        double P = exp(sc * dot - m[gr]) / l[gr];
+                        double dS = P * (dP - Dr[gr]);
+                        for (int c = 0; c < d; ++c)
+                            acc[c] += dS * kd[j * d + c];
+                    }
+                    for (int c = 0; c < d; ++c)
+                        dq[t * d + c] = sc * acc[c];
+                }
+                free(acc);
+            }
+
+            /* 3. dv_j = sum P_ij dO_i and dk_j = scale * sum dS_ij q_i over the
+             *    group's query heads and the rows that see j */
+#pragma omp parallel num_threads(threads)
+            {
+                double *ak = malloc(sizeof(double) * (size_t)d);
+                double *av = malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(dynamic, 8)
+                for (int64_t t = 0; t < n_kv_rows; ++t) {
+                    int64_t r = kv_rows ? kv_rows[t] : t;
+                    if (r / L != (int64_t)b * H_kv + g)
+                        continue;
+                    const int64_t j = r % L;
+                    const double *kj = kd + j * d, *vj = vd + j * d;
+                    for (int c = 0; c < d; ++c)
+                        ak[c] = av[c] = 0.0;
+                    for (int hh = 0; hh < group; ++hh) {
+                        for (int64_t i = 0; i < L; ++i) {
+                            if (!oracle_visible(i, j, causal, window))
+                                continue;
+                            const int64_t gr = hh * L + i;
+                            const double *qi = qd + gr * d, *doi = dod + gr * d;
+                            double dot = 0.0, dP = 0.0;
+                            for (int c = 0; c < d; ++c) {
+                                dot += qi[c] * kj[c];
+                                dP += doi[c] * vj[c];
+                            }
+                            double P = exp(sc * dot - m[gr]) / l[gr];
+                            double dS = P * (dP - Dr[gr]);
+                            for (int c = 0; c < d; ++c) {
+                                av[c] += P * doi[c];
+                                ak[c] += dS * qi[c];
+                            }
+                        }
+                    }
+                    for (int c = 0; c < d; ++c) {
+                        dv[t * d + c] = av[c];
+                        dk[t * d + c] = sc * ak[c];
+                    }
+                }
+                free(ak);
+                free(av);
+            }
+        }
+    }
+    free(kd);
+    free(vd);
+    free(qd);
+    free(dod);
+    free(m);
+    free(l);
+    free(Dr);
+    free(needed);
     return status;
 }

@@ -10,6 +10,7 @@ import os
 import pytest
 
 import oracle
+import oracle_bwd_pins
 import oracle_pins
 
 MUTANTS = {
@@ -28,6 +29,17 @@ MUTANTS = {
     "default_scale_wrong": ("return (float)(1.0 / sqrt((double)d));", "return (float)(1.0 / (double)d);"),
     "max_not_subtracted_from_lse_side": ("double p = exp(s[j] - m);", "double p = exp(s[j]);"),
     "sum_over_one_row_only": ("l += p;", "l = p;"),
+    # backward pass
+    "bwd_dq_uses_values": ("acc[c] += dS * kd[j * d + c];", "acc[c] += dS * vd[j * d + c];"),
+    "bwd_dq_scale_dropped": ("dq[t * d + c] = sc * acc[c];", "dq[t * d + c] = acc[c];"),
+    "bwd_dk_scale_dropped": ("dk[t * d + c] = sc * ak[c];", "dk[t * d + c] = ak[c];"),
+    "bwd_dv_unnormalised": ("av[c] += P * doi[c];", "av[c] += P * l[gr] * doi[c];"),
+    "bwd_delta_unnormalised": ("D += dod[c] * (acc[c] / l);", "D += dod[c] * acc[c];"),
+    "bwd_dk_sign": ("ak[c] += dS * qi[c];", "ak[c] -= dS * qi[c];"),
+    "bwd_dk_reads_first_head": ("const int64_t gr = hh * L + i;", "const int64_t gr = i;"),
+    "bwd_group_heads_dropped": ("for (int hh = 0; hh < group; ++hh) {", "for (int hh = 0; hh < 1; ++hh) {"),
+    "bwd_stats_rows_skipped": ("needed[hh * L + i] = 1;", "needed[hh * L + i] = needed[hh * L + i];"),
+    "bwd_dq_row_of_first_head": ("const int64_t gr = (bh % H - h0) * L + r % L;", "const int64_t gr = r % L;"),
 }
 
 
@@ -41,7 +53,7 @@ def test_planted_mistake_is_caught(name, tmp_path):
         f.write(src.replace(old, new))
     lib = oracle.load_library(oracle.compile_library(path, os.path.join(tmp_path, "mutant.so")))
     caught = []
-    for pin in oracle_pins.ALL_PINS:
+    for pin in oracle_pins.ALL_PINS + oracle_bwd_pins.ALL_BWD_PINS:
         try:
             pin(lib)
         except (AssertionError, ValueError) as exc:

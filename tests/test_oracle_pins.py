@@ -1,11 +1,17 @@
 """The fp64 oracle against its pins (CPU only)."""
 import pytest
 
+import oracle_bwd_pins
 import oracle_pins
 
 
 @pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda f: f.__name__)
 def test_pin(pin, oracle_lib):
+    pin(oracle_lib)
+
+
+@pytest.mark.parametrize("pin", oracle_bwd_pins.ALL_BWD_PINS, ids=lambda f: f.__name__)
+def test_bwd_pin(pin, oracle_lib):
     pin(oracle_lib)
 
 

@@ -70,7 +70,7 @@ def _bind(lib):
                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int, ctypes.c_float,
                                     i64p, ctypes.c_int64, i64p, ctypes.c_int64,
-                                    f64p, f64p, f64p, ctypes.c_int]
+                                    f64p, f64p, f64p, f64p, f64p, f64p, f64p, f64p, ctypes.c_int]
     lib.oracle_decode.restype = None
     lib.oracle_decode.argtypes = [u16p, f64p, ctypes.c_int64, ctypes.c_int]
     lib.oracle_resolve_scale.restype = ctypes.c_float
@@ -174,7 +174,7 @@ def _row_ids(rows, total):
 
 
 def attention_bwd(q, k, v, dout, dtype: str, causal: bool, window: int = -1, scale: float = 0.0,
-                  q_rows=None, kv_rows=None, threads: int = 0, lib=None):
+                  q_rows=None, kv_rows=None, threads: int = 0, lib=None, with_abs: bool = False):
     """Gradients of exact attention of 16-bit inputs, in fp64.
 
     q, dout: [B,H,L,d]; k, v: [B,H_kv,L,d] (torch tensors or uint16 arrays of
@@ -182,7 +182,13 @@ def attention_bwd(q, k, v, dout, dtype: str, causal: bool, window: int = -1, sca
     rows wanted; ``kv_rows``: optional flat ids (b*H_kv + g)*L + j of the
     dk/dv rows wanted (an empty list skips that part).
     Returns (dq, dk, dv): fp64 [B,H,L,d], [B,H_kv,L,d], [B,H_kv,L,d], or
-    [n_q, d], [n_kv, d], [n_kv, d] for the requested rows.
+    [n_q, d], [n_kv, d], [n_kv, d] for the requested rows.  With
+    ``with_abs``, returns ((dq, dk, dv), (dq_abs, dk_abs, dv_abs),
+    (dq_dsens, dk_dsens)): the second triple holds, for each element, the sum
+    of the absolute values of the terms whose sum it is; the third, the
+    sensitivity of dq and dk to the row terms D_i = dO_i.O_i (if each D_i
+    moves by at most eps times the root-sum-square of its terms, the element
+    moves by at most eps times this).
     """
     lib = lib or _default_lib()
     qb, kb, vb, gb = _bits(q), _bits(k), _bits(v), _bits(dout)
@@ -195,15 +201,29 @@ def attention_bwd(q, k, v, dout, dtype: str, causal: bool, window: int = -1, sca
     dq = np.zeros((nq, d), np.float64)
     dk = np.zeros((nk, d), np.float64)
     dv = np.zeros((nk, d), np.float64)
+    absd = [np.zeros_like(dq), np.zeros_like(dk), np.zeros_like(dv)] if with_abs else [None] * 3
+    sens = [np.zeros_like(dq), np.zeros_like(dk)] if with_abs else [None] * 2
+    aptr = [_ptr(a, ctypes.c_double) if a is not None else None for a in absd + sens]
     st = lib.oracle_attn_bwd(_ptr(qb, ctypes.c_uint16), _ptr(kb, ctypes.c_uint16), _ptr(vb, ctypes.c_uint16),
                              _ptr(gb, ctypes.c_uint16), DTYPES[dtype], B, H, H_kv, L, d,
                              int(bool(causal)), int(window), float(scale), qp, nq, kp, nk,
                              _ptr(dq, ctypes.c_double), _ptr(dk, ctypes.c_double),
-                             _ptr(dv, ctypes.c_double), int(threads))
+                             _ptr(dv, ctypes.c_double), *aptr, int(threads))
     if st != 0:
         raise ValueError(f"oracle_attn_bwd failed with status {st}")
+    grads = [dq, dk, dv]
     if q_rows is None:
-        dq = dq.reshape(B, H, L, d)
+        grads[0] = dq.reshape(B, H, L, d)
+        if with_abs:
+            absd[0] = absd[0].reshape(B, H, L, d)
+            sens[0] = sens[0].reshape(B, H, L, d)
     if kv_rows is None:
-        dk, dv = dk.reshape(B, H_kv, L, d), dv.reshape(B, H_kv, L, d)
-    return dq, dk, dv
+        for i in (1, 2):
+            grads[i] = grads[i].reshape(B, H_kv, L, d)
+            if with_abs:
+                absd[i] = absd[i].reshape(B, H_kv, L, d)
+        if with_abs:
+            sens[1] = sens[1].reshape(B, H_kv, L, d)
+    if with_abs:
+        return tuple(grads), tuple(absd), tuple(sens)
+    return tuple(grads)

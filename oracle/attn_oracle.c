@@ -130,11 +130,13 @@ static int reads_kv_head(int64_t r, int b, int g, int H, int H_kv, int L)
  * their maximum m, l = sum_j exp(s_ij - m), and acc = sum_j exp(s_ij - m) v_j
  * (so O_i = acc / l).  qd: the row's decoded q; kd, vd: the decoded K/V head.
  * If dod (the row's decoded upstream gradient) is not NULL, also
- * D = dO_i . O_i for the backward pass.  Returns 0, or -2 if the row sees no
+ * D = dO_i . O_i for the backward pass, and rho = sqrt(sum_c (dO_ic O_ic)^2),
+ * the root-sum-square of D's terms.  Returns 0, or -2 if the row sees no
  * key. */
 static int row_softmax(const double *qd, const double *dod, const double *kd, const double *vd,
                        int64_t i, int L, int d, int causal, int window, double sc,
-                       double *s, double *acc, double *m_out, double *l_out, double *D_out)
+                       double *s, double *acc, double *m_out, double *l_out, double *D_out,
+                       double *rho_out)
 {
     double m = -INFINITY;
     int64_t count = 0;
@@ -165,10 +167,13 @@ static int row_softmax(const double *qd, const double *dod, const double *kd, co
     *m_out = m;
     *l_out = l;
     if (dod) {
-        double D = 0.0;
-        for (int c = 0; c < d; ++c)
+        double D = 0.0, R = 0.0;
+        for (int c = 0; c < d; ++c) {
             D += dod[c] * (acc[c] / l);
+            R += (dod[c] * (acc[c] / l)) * (dod[c] * (acc[c] / l));
+        }
         *D_out = D;
+        *rho_out = sqrt(R);
     }
     return 0;
 }
@@ -236,7 +241,7 @@ int oracle_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v, int dty
 
                     double m, l;
                     if (row_softmax(qd, NULL, kd, vd, i, L, d, causal, window, sc, s, acc, &m, &l,
-                                    NULL) != 0) {
+                                    NULL, NULL) != 0) {
 #pragma omp atomic write
                         status = -2;
                         continue;
@@ -285,12 +290,24 @@ int oracle_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v, int dty
  *   (then n_q_rows is ignored); dq: [n_q_rows, d].
  * kv_rows: flat ids (b*H_kv + g)*L + j of the dk/dv rows wanted, or NULL for
  *   all; dk, dv: [n_kv_rows, d].
+ * dq_abs, dk_abs, dv_abs: NULL, or arrays shaped like dq, dk, dv that receive
+ *   the sum of the absolute values of the terms whose sum is each gradient
+ *   element (scale * sum_j |dS_ij k_j|, scale * sum |dS_ij q_i|,
+ *   sum |P_ij dO_i|): the size a rounding error relative to each term can
+ *   reach, used by tests to bound 16-bit arithmetic.
+ * dq_dsens, dk_dsens: NULL, or arrays shaped like dq, dk that receive the
+ *   sensitivity of each element to the row terms D: scale * rho_i *
+ *   sum_j P_ij |k_j| and scale * sum_i P_ij rho_i |q_i|, with rho_i the
+ *   root-sum-square of the terms of D_i.  If every D_i moves by at most
+ *   eps * rho_i, dq and dk move by at most eps times these.
  * Returns 0, -1 for bad arguments or no memory, -2 if a row has no visible key.
  */
 int oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *dout,
                     int dtype, int B, int H, int H_kv, int L, int d, int causal, int window,
                     float scale, const int64_t *q_rows, int64_t n_q_rows, const int64_t *kv_rows,
-                    int64_t n_kv_rows, double *dq, double *dk, double *dv, int threads)
+                    int64_t n_kv_rows, double *dq, double *dk, double *dv, double *dq_abs,
+                    double *dk_abs, double *dv_abs, double *dq_dsens, double *dk_dsens,
+                    int threads)
 {
     if (B < 0 || H <= 0 || H_kv <= 0 || L < 0 || d <= 0 || H % H_kv != 0 || window < -1)
         return -1;
@@ -314,9 +331,10 @@ int oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
     double *m = malloc(sizeof(double) * (size_t)group_rows);
     double *l = malloc(sizeof(double) * (size_t)group_rows);
     double *Dr = malloc(sizeof(double) * (size_t)group_rows);
+    double *rho = malloc(sizeof(double) * (size_t)group_rows);
     char *needed = malloc((size_t)group_rows);
     int status = 0;
-    if (!kd || !vd || !qd || !dod || !m || !l || !Dr || !needed)
+    if (!kd || !vd || !qd || !dod || !m || !l || !Dr || !rho || !needed)
         status = -1;
 
     for (int b = 0; b < B && status == 0; ++b) {
@@ -366,7 +384,7 @@ int oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
                     if (!needed[r])
                         continue;
                     if (row_softmax(qd + r * d, dod + r * d, kd, vd, r % L, L, d, causal, window, sc,
-                                  s, acc, &m[r], &l[r], &Dr[r]) != 0) {
+                                  s, acc, &m[r], &l[r], &Dr[r], &rho[r]) != 0) {
 #pragma omp atomic write
                         status = -2;
                     }
@@ -381,6 +399,8 @@ int oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
 #pragma omp parallel num_threads(threads)
             {
                 double *acc = malloc(sizeof(double) * (size_t)d);
+                double *acc_abs = malloc(sizeof(double) * (size_t)d);
+                double *acc_P = malloc(sizeof(double) * (size_t)d);
 #pragma omp for schedule(dynamic, 8)
                 for (int64_t t = 0; t < n_q_rows; ++t) {
                     int64_t r = q_rows ? q_rows[t] : t;
@@ -391,7 +411,7 @@ int oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
                     const int64_t i = r % L;
                     const double *qi = qd + gr * d, *doi = dod + gr * d;
                     for (int c = 0; c < d; ++c)
-                        acc[c] = 0.0;
+                        acc[c] = acc_abs[c] = acc_P[c] = 0.0;
                     for (int64_t j = 0; j < L; ++j) {
                         if (!oracle_visible(i, j, causal, window))
                             continue;
@@ -402,13 +422,23 @@ int oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
                         }
                         double P = exp(sc * dot - m[gr]) / l[gr];
                         double dS = P * (dP - Dr[gr]);
-                        for (int c = 0; c < d; ++c)
+                        for (int c = 0; c < d; ++c) {
                             acc[c] += dS * kd[j * d + c];
+                            acc_abs[c] += fabs(dS * kd[j * d + c]);
+                            acc_P[c] += P * fabs(kd[j * d + c]);
+                        }
                     }
-                    for (int c = 0; c < d; ++c)
+                    for (int c = 0; c < d; ++c) {
                         dq[t * d + c] = sc * acc[c];
+                        if (dq_abs)
+                            dq_abs[t * d + c] = sc * acc_abs[c];
+                        if (dq_dsens)
+                            dq_dsens[t * d + c] = sc * rho[gr] * acc_P[c];
+                    }
                 }
                 free(acc);
+                free(acc_abs);
+                free(acc_P);
             }
 
             /* 3. dv_j = sum P_ij dO_i and dk_j = scale * sum dS_ij q_i over the
@@ -417,6 +447,9 @@ int oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
             {
                 double *ak = malloc(sizeof(double) * (size_t)d);
                 double *av = malloc(sizeof(double) * (size_t)d);
+                double *ak_abs = malloc(sizeof(double) * (size_t)d);
+                double *av_abs = malloc(sizeof(double) * (size_t)d);
+                double *ak_P = malloc(sizeof(double) * (size_t)d);
 #pragma omp for schedule(dynamic, 8)
                 for (int64_t t = 0; t < n_kv_rows; ++t) {
                     int64_t r = kv_rows ? kv_rows[t] : t;
@@ -425,7 +458,7 @@ int oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
                     const int64_t j = r % L;
                     const double *kj = kd + j * d, *vj = vd + j * d;
                     for (int c = 0; c < d; ++c)
-                        ak[c] = av[c] = 0.0;
+                        ak[c] = av[c] = ak_abs[c] = av_abs[c] = ak_P[c] = 0.0;
                     for (int hh = 0; hh < group; ++hh) {
                         for (int64_t i = 0; i < L; ++i) {
                             if (!oracle_visible(i, j, causal, window))
@@ -442,16 +475,28 @@ int oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
                             for (int c = 0; c < d; ++c) {
                                 av[c] += P * doi[c];
                                 ak[c] += dS * qi[c];
+                                av_abs[c] += fabs(P * doi[c]);
+                                ak_abs[c] += fabs(dS * qi[c]);
+                                ak_P[c] += P * rho[gr] * fabs(qi[c]);
                             }
                         }
                     }
                     for (int c = 0; c < d; ++c) {
                         dv[t * d + c] = av[c];
                         dk[t * d + c] = sc * ak[c];
+                        if (dk_abs) {
+                            dv_abs[t * d + c] = av_abs[c];
+                            dk_abs[t * d + c] = sc * ak_abs[c];
+                        }
+                        if (dk_dsens)
+                            dk_dsens[t * d + c] = sc * ak_P[c];
                     }
                 }
                 free(ak);
                 free(av);
+                free(ak_abs);
+                free(av_abs);
+                free(ak_P);
             }
         }
     }
@@ -462,6 +507,7 @@ int oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
     free(m);
     free(l);
     free(Dr);
+    free(rho);
     free(needed);
     return status;
 }

@@ -16,9 +16,12 @@ disagree with what mathematics fixes:
   sum_i dO_i.O_i;
 * closed forms: one visible key gives dq = dk = 0 and dv = dO; K = 0 gives
   dq = 0 and dv_j = sum over rows seeing j of dO_i / |V(i)|; two visible keys
-  give the derivative of a sigmoid mix;
+  give the derivative of a sigmoid mix (and the sum of |terms| of dq);
 * relations: doubling the scale vs doubling q, GQA vs K/V heads repeated to
-  H, rows requested one by one vs all at once.
+  H, rows requested one by one vs all at once;
+* the sums of |terms| returned beside the gradients bound them, and equal
+  them where every term has one sign; they and the sensitivities to the row
+  terms D are pinned in closed form by the two-key case.
 """
 from __future__ import annotations
 
@@ -180,17 +183,44 @@ def pin_bwd_zero_keys(lib, L=200, d=64):
 
 def pin_bwd_two_keys(lib):
     """Causal window 1: row i >= 1 sees keys i-1 and i with weight
-    sigma = 1/(1+exp(s_{i,i-1} - s_{i,i})) on key i, and
-    dq_i = scale * sigma (1-sigma) (dO_i.(v_i - v_{i-1})) (k_i - k_{i-1})."""
+    sigma = 1/(1+exp(s_{i,i-1} - s_{i,i})) on key i, so
+    dS_{i,i} = -dS_{i,i-1} = sigma (1-sigma) (dO_i.(v_i - v_{i-1})) and
+    dq_i = scale dS_{i,i} (k_i - k_{i-1}); each key is seen by two rows, which
+    gives dk, dv and all the sums of |terms| in closed form too."""
     q, k, v, dout = _inputs(1, 1, 1, 40, 64, "f16", 44)
     scale = 0.125
-    dq, _, _ = _bwd(lib, q, k, v, dout, "f16", True, 1, scale)
+    (dq, dk, dv), (dq_abs, dk_abs, dv_abs), (dq_sens, dk_sens) = _bwd(lib, q, k, v, dout, "f16", True, 1,
+                                                                     scale, with_abs=True)
     qf, kf, vf, gf = (_f64(t)[0, 0] for t in (q, k, v, dout))
+    sig_of, ds_of = {0: 1.0}, {0: 0.0, 40: 0.0}  # row 0 sees key 0 only; row 40 does not exist
+    rho_of = {0: np.linalg.norm(gf[0] * vf[0]), 40: 0.0}  # root-sum-square of the terms of D_i
     for i in range(1, 40):
         s_new, s_old = scale * qf[i] @ kf[i], scale * qf[i] @ kf[i - 1]
         sig = 1.0 / (1.0 + math.exp(s_old - s_new))
-        want = scale * sig * (1 - sig) * (gf[i] @ (vf[i] - vf[i - 1])) * (kf[i] - kf[i - 1])
+        ds = sig * (1 - sig) * (gf[i] @ (vf[i] - vf[i - 1]))  # dS of key i; key i-1 gets -ds
+        want = scale * ds * (kf[i] - kf[i - 1])
         assert np.max(np.abs(dq[0, 0, i] - want)) <= 1e-12, f"row {i}"
+        want_abs = scale * abs(ds) * (np.abs(kf[i]) + np.abs(kf[i - 1]))
+        assert np.max(np.abs(dq_abs[0, 0, i] - want_abs)) <= 1e-12, f"|terms| of row {i}"
+        rho = np.linalg.norm(gf[i] * (sig * vf[i] + (1 - sig) * vf[i - 1]))
+        want_sens = scale * rho * (sig * np.abs(kf[i]) + (1 - sig) * np.abs(kf[i - 1]))
+        assert np.max(np.abs(dq_sens[0, 0, i] - want_sens)) <= 1e-12, f"D sensitivity of row {i}"
+        sig_of[i], ds_of[i], rho_of[i] = sig, ds, rho
+    # key j is seen by rows j (weight sigma_j, dS = ds_j) and j+1 (weight
+    # 1 - sigma_{j+1}, dS = -ds_{j+1})
+    for j in range(40):
+        s_next = sig_of.get(j + 1, 1.0)
+        want = sig_of[j] * gf[j] + (1 - s_next) * (gf[j + 1] if j + 1 < 40 else 0)
+        assert np.max(np.abs(dv[0, 0, j] - want)) <= 1e-12, f"dv of key {j}"
+        want = sig_of[j] * np.abs(gf[j]) + (1 - s_next) * (np.abs(gf[j + 1]) if j + 1 < 40 else 0)
+        assert np.max(np.abs(dv_abs[0, 0, j] - want)) <= 1e-12, f"|terms| of dv of key {j}"
+        q_next = qf[j + 1] if j + 1 < 40 else 0 * qf[j]
+        want = scale * (ds_of[j] * qf[j] - ds_of[j + 1] * q_next)
+        assert np.max(np.abs(dk[0, 0, j] - want)) <= 1e-12, f"dk of key {j}"
+        want = scale * (abs(ds_of[j]) * np.abs(qf[j]) + abs(ds_of[j + 1]) * np.abs(q_next))
+        assert np.max(np.abs(dk_abs[0, 0, j] - want)) <= 1e-12, f"|terms| of dk of key {j}"
+        want = scale * (sig_of[j] * rho_of[j] * np.abs(qf[j]) + (1 - s_next) * rho_of[j + 1] * np.abs(q_next))
+        assert np.max(np.abs(dk_sens[0, 0, j] - want)) <= 1e-12, f"D sensitivity of dk of key {j}"
 
 
 # ---------------------------------------------------------------- relations
@@ -235,3 +265,29 @@ ALL_BWD_PINS = [
     pin_bwd_causal_row0, pin_bwd_zero_keys, pin_bwd_two_keys, pin_bwd_scale_vs_query,
     pin_bwd_gqa_equals_repeated_heads, pin_bwd_row_subsets,
 ]
+
+
+def pin_bwd_abs_sums(lib):
+    """The sums of |terms| bound their sums, reduce to them where every term
+    has one sign (dv with non-negative dO: P >= 0), and do not change the
+    gradients."""
+    q, k, v, dout = _inputs(1, 4, 2, 60, 64, "f16", 48)
+    g, a, _ = _bwd(lib, q, k, v, dout, "f16", True, 9, 0.125, with_abs=True)
+    plain = _bwd(lib, q, k, v, dout, "f16", True, 9, 0.125)
+    for x, y, s in zip(g, plain, a):
+        assert np.array_equal(x, y)
+        assert np.all(np.abs(x) <= s * (1 + 1e-12))
+    pos = dout.abs()
+    g, a, _ = _bwd(lib, q, k, v, pos, "f16", True, 9, 0.125, with_abs=True)
+    assert np.max(np.abs(g[2] - a[2])) <= 1e-12 * (1 + np.max(a[2]))
+    gs, as_, ss = _bwd(lib, q, k, v, dout, "f16", True, 9, 0.125, q_rows=[3, 100], kv_rows=[7, 64],
+                       with_abs=True)
+    full, full_abs, full_sens = _bwd(lib, q, k, v, dout, "f16", True, 9, 0.125, with_abs=True)
+    assert np.array_equal(ss[0], full_sens[0].reshape(-1, 64)[[3, 100]])
+    assert np.array_equal(ss[1], full_sens[1].reshape(-1, 64)[[7, 64]])
+    assert np.array_equal(as_[0], full_abs[0].reshape(-1, 64)[[3, 100]])
+    assert np.array_equal(as_[1], full_abs[1].reshape(-1, 64)[[7, 64]])
+    assert np.array_equal(as_[2], full_abs[2].reshape(-1, 64)[[7, 64]])
+
+
+ALL_BWD_PINS.append(pin_bwd_abs_sums)

@@ -40,6 +40,12 @@ MUTANTS = {
     "bwd_group_heads_dropped": ("for (int hh = 0; hh < group; ++hh) {", "for (int hh = 0; hh < 1; ++hh) {"),
     "bwd_stats_rows_skipped": ("needed[hh * L + i] = 1;", "needed[hh * L + i] = needed[hh * L + i];"),
     "bwd_dq_row_of_first_head": ("const int64_t gr = (bh % H - h0) * L + r % L;", "const int64_t gr = r % L;"),
+    "bwd_abs_dv_signed": ("av_abs[c] += fabs(P * doi[c]);", "av_abs[c] += P * doi[c];"),
+    "bwd_abs_dq_without_key": ("acc_abs[c] += fabs(dS * kd[j * d + c]);", "acc_abs[c] += fabs(dS);"),
+    "bwd_abs_dk_unscaled": ("dk_abs[t * d + c] = sc * ak_abs[c];", "dk_abs[t * d + c] = ak_abs[c];"),
+    "bwd_rho_not_rooted": ("*rho_out = sqrt(R);", "*rho_out = R;"),
+    "bwd_dsens_dk_without_weight": ("ak_P[c] += P * rho[gr] * fabs(qi[c]);", "ak_P[c] += rho[gr] * fabs(qi[c]);"),
+    "bwd_dsens_dq_without_rho": ("dq_dsens[t * d + c] = sc * rho[gr] * acc_P[c];", "dq_dsens[t * d + c] = sc * acc_P[c];"),
 }
 
 

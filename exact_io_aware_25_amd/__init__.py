@@ -1,13 +1,13 @@
-"""Exact IO-aware attention forward for AMD MI355X (gfx950).
+"""Exact IO-aware attention (forward and backward) for AMD MI355X (gfx950).
 
 A thin ctypes binding over the C ABI declared in ``include/attn.h``.  The
 names match the C entry points; this module only marshals arguments.  Every
 step of the computation runs in the HIP kernels of ``libattn_gfx950.so``;
 there is no fallback: if the library is missing, every call raises.
 
-``forward`` is a convenience for PyTorch users: it checks the tensors,
-allocates ``out`` and ``lse`` with torch on the inputs' device and launches
-on torch's current stream.
+``forward`` and ``backward`` are conveniences for PyTorch users: they check
+the tensors, allocate the outputs (and the backward's workspace) with torch
+on the inputs' device and launch on torch's current stream.
 """
 from __future__ import annotations
 
@@ -29,7 +29,8 @@ ATTN_ERR_FLAG = 8
 ATTN_ERR_SCALE = 9
 ATTN_ERR_ALIGN = 10
 
-EXPORTS = ("attn_fwd", "attn_fwd_bf16", "attn_launch_shape", "attn_status_string", "attn_resolve_scale")
+EXPORTS = ("attn_fwd", "attn_fwd_bf16", "attn_bwd", "attn_bwd_bf16", "attn_bwd_workspace_size",
+           "attn_launch_shape", "attn_status_string", "attn_resolve_scale")
 
 _lib = None
 
@@ -57,6 +58,13 @@ def library():
             fn = getattr(lib, name)
             fn.restype = ctypes.c_int
             fn.argtypes = sig
+        bsig = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 7 + [ctypes.c_float, ctypes.c_void_p]
+        for name in ("attn_bwd", "attn_bwd_bf16"):
+            fn = getattr(lib, name)
+            fn.restype = ctypes.c_int
+            fn.argtypes = bsig
+        lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
+        lib.attn_bwd_workspace_size.argtypes = [ctypes.c_int] * 3
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.attn_status_string.argtypes = [ctypes.c_int]
         lib.attn_resolve_scale.restype = ctypes.c_float
@@ -75,6 +83,24 @@ def attn_fwd(q, k, v, out, lse, B, H, H_kv, L, d, causal, window, scale, stream)
 def attn_fwd_bf16(q, k, v, out, lse, B, H, H_kv, L, d, causal, window, scale, stream) -> int:
     """bf16 entry point; same arguments as ``attn_fwd``."""
     return library().attn_fwd_bf16(q, k, v, out, lse, B, H, H_kv, L, d, causal, window, scale, stream)
+
+
+def attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, workspace, B, H, H_kv, L, d, causal, window, scale,
+             stream) -> int:
+    """fp16 backward entry point; pointers are integer device addresses."""
+    return library().attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, workspace, B, H, H_kv, L, d, causal,
+                              window, scale, stream)
+
+
+def attn_bwd_bf16(q, k, v, out, dout, lse, dq, dk, dv, workspace, B, H, H_kv, L, d, causal, window, scale,
+                  stream) -> int:
+    """bf16 backward entry point; same arguments as ``attn_bwd``."""
+    return library().attn_bwd_bf16(q, k, v, out, dout, lse, dq, dk, dv, workspace, B, H, H_kv, L, d, causal,
+                                   window, scale, stream)
+
+
+def attn_bwd_workspace_size(B, H, L) -> int:
+    return int(library().attn_bwd_workspace_size(int(B), int(H), int(L)))
 
 
 def attn_status_string(status: int) -> str:
@@ -133,8 +159,63 @@ def forward(q, k, v, causal: bool = False, window: int = -1, scale=None, out=Non
         status = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                     B, H, H_kv, L, d, int(bool(causal)), int(window),
                     0.0 if scale is None else float(scale), stream.cuda_stream)
-    if status != ATTN_OK:
-        exc = ValueError if status in (1, 2, 3, 4, 5, 8, 9, 10) else AttnError
-        msg = attn_status_string(status)
-        raise exc(msg) if exc is ValueError else exc(status, msg)
+    _check(status)
     return out, lse
+
+
+def _check(status):
+    if status != ATTN_OK:
+        msg = attn_status_string(status)
+        if status in (1, 2, 3, 4, 5, 8, 9, 10):
+            raise ValueError(msg)
+        raise AttnError(status, msg)
+
+
+def backward(q, k, v, out, lse, dout, causal: bool = False, window: int = -1, scale=None,
+             dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of attention for the upstream gradient ``dout``.
+
+    q, k, v, causal, window, scale as given to ``forward``; out and lse as it
+    returned them; dout like out.  Outputs are allocated unless given;
+    ``workspace`` (uint8, ``attn_bwd_workspace_size`` bytes) likewise.
+    Launches on ``stream`` (default: torch's current stream).
+    """
+    import torch
+
+    tensors = (q, k, v, out, dout)
+    if any(t.dim() != 4 for t in tensors):
+        raise ValueError("q, k, v, out, dout must be 4-D")
+    if q.dtype not in (torch.float16, torch.bfloat16) or any(t.dtype != q.dtype for t in tensors):
+        raise ValueError("q, k, v, out, dout must share one dtype, float16 or bfloat16")
+    if not q.is_cuda or any(t.device != q.device for t in tensors + (lse,)):
+        raise ValueError("all tensors must be on the same GPU device")
+    if not all(t.is_contiguous() for t in tensors + (lse,)):
+        raise ValueError("all tensors must be contiguous")
+    B, H, L, d = q.shape
+    H_kv = k.shape[1]
+    if (tuple(k.shape) != (B, H_kv, L, d) or tuple(v.shape) != tuple(k.shape)
+            or tuple(out.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape)):
+        raise ValueError("shape mismatch between q, k, v, out, dout")
+    if tuple(lse.shape) != (B, H, L) or lse.dtype != torch.float32:
+        raise ValueError("lse must be a float32 tensor [B, H, L]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        if (tuple(t.shape) != tuple(like.shape) or t.dtype != like.dtype or not t.is_contiguous()
+                or t.device != q.device):
+            raise ValueError(f"{name} must be a contiguous tensor like {name[1:]}")
+    need = attn_bwd_workspace_size(B, H, L)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if workspace.numel() * workspace.element_size() < need or workspace.device != q.device:
+        raise ValueError(f"workspace must hold {need} bytes on q's device")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    fn = attn_bwd if q.dtype == torch.float16 else attn_bwd_bf16
+    with torch.cuda.device(q.device):
+        status = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                    dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), B, H, H_kv, L, d,
+                    int(bool(causal)), int(window), 0.0 if scale is None else float(scale), stream.cuda_stream)
+    _check(status)
+    return dq, dk, dv

@@ -1,0 +1,674 @@
+// attn_bwd.hip -- exact attention backward pass for MI355X (CDNA4, gfx950).
+//
+// The gradients of O = softmax(scale * Q K^T + mask) V with respect to q, k
+// and v for an upstream gradient dO.  The pages recommend the method for
+// training as well as inference («Оптимизация внимания Flash», introduction)
+// and list the backward pass as unmeasured («ТЕХНИЧЕСКОЕ ЗАДАНИЕ: Сравнить
+// Hyena vs FlashAttention на 128k», stage 5); the computation is the
+// gradient of the forward definition, done the same IO-aware way: the
+// softmax weights are recomputed tile by tile from the forward's logsumexp,
+// so no L x L matrix reaches device memory.  With P_ij = exp(s_ij - lse_i):
+//
+//   D_i   = dO_i . O_i
+//   dS_ij = P_ij (dO_i . v_j - D_i)
+//   dv_j  = sum_i P_ij dO_i,  dk_j = scale sum_i dS_ij q_i,  dq_i = scale sum_j dS_ij k_j
+//
+// Three kernels on the caller's stream:
+//   1. prep: per query row, -lse*log2(e) and D into the workspace;
+//   2. dK/dV: a workgroup owns 32*NW keys of one K/V head and walks the
+//      query tiles of every query head that reads it.  K and V fragments stay
+//      in registers (B operands); Q and dO tiles stream through LDS.  Per
+//      32-query block: S = Q K^T and dP = dO V^T (query rows fed in the
+//      bit-2/3-swapped order, so the rounded registers are directly the B
+//      operands of the next products), P and dS elementwise, then
+//      dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T from transposing
+//      LDS reads;
+//   3. dQ: a workgroup owns 32*NW query rows, like the forward; Q^T and dO^T
+//      fragments stay in registers; K and V tiles stream through LDS.  Per
+//      64-key tile: S^T = K Q^T, dP^T = V dO^T, dS^T, then dQ^T += K^T dS^T
+//      with K^T from transposing LDS reads.
+// No atomics: every output element is written once, by one lane, so the
+// result is deterministic.  The price is that S and dP are computed twice
+// (once per kernel): 7 products per visible pair instead of 5.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "attn.h"
+#include "attn_common.h"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kTileQ = 64;  // query rows per LDS tile of the dK/dV kernel
+
+struct BwdParams {
+    const void *q, *k, *v, *o, *dout;
+    const float *lse;
+    float *ws;          // per (b, h): Lp floats of -lse*log2(e), then Lp floats of D
+    void *dq, *dk, *dv;
+    int B, H, H_kv, L;
+    int Lp;             // L rounded up to a multiple of kTileQ
+    int group;          // H / H_kv
+    int window;         // -1 or the window size
+    int n_blk;          // blocks of the launched kernel along L
+    float scale;        // resolved softmax scale
+    float scale_log2;   // scale * log2(e)
+};
+
+// ---------------------------------------------------------------- 1. prep
+// One row of D/8 16-byte pieces per D/8 consecutive lanes.  Rows L..Lp-1 of
+// each (b, h) get zeros, so every workspace value the dK/dV kernel can read
+// is finite.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdParams p)
+{
+    typedef typename Vec8<T>::type vec8;
+    constexpr int kPieces = D / 8;
+    constexpr int kRowsPerBlock = 256 / kPieces;
+    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kPieces;  // over B*H*Lp
+    const int piece = threadIdx.x % kPieces;
+    const int64_t bh = row / p.Lp;
+    const int i = (int)(row % p.Lp);
+    const bool live = bh < (int64_t)p.B * p.H && i < p.L;
+    float acc = 0.f;
+    if (live) {
+        const int64_t off = (bh * p.L + i) * D + 8 * piece;
+        const vec8 o = *reinterpret_cast<const vec8 *>(static_cast<const T *>(p.o) + off);
+        const vec8 g = *reinterpret_cast<const vec8 *>(static_cast<const T *>(p.dout) + off);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf((float)o[e], (float)g[e], acc);
+    }
+#pragma unroll
+    for (int off = kPieces / 2; off > 0; off /= 2) acc += __shfl_xor(acc, off);
+    if (piece == 0 && bh < (int64_t)p.B * p.H) {
+        float *w = p.ws + bh * 2 * p.Lp;
+        w[i] = live ? -p.lse[bh * p.L + i] * kLog2e : 0.f;
+        w[p.Lp + i] = acc;
+    }
+}
+
+// ---------------------------------------------------------------- 2. dK, dV
+template <typename T, int D, bool CAUSAL, bool WINDOW, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_bwd_dkdv_kernel(BwdParams p)
+{
+    typedef typename Vec8<T>::type vec8;
+    constexpr int kThreads = 64 * NW;
+    constexpr int kBlockKV = kRowsPerWave * NW;          // keys per workgroup
+    constexpr int kRowBytes = 2 * D;
+    constexpr int kTileBytes = kTileQ * kRowBytes;       // one Q or dO tile
+    constexpr int kWsBytes = 1024;                       // -lse*log2e and D of 64 rows, + zero fill
+    constexpr int kStageBytes = 2 * kTileBytes + kWsBytes;
+    constexpr int kUnits = D / 8;
+    constexpr int kChunks = kTileQ * kUnits / kThreads;  // 16-byte units per thread per tile
+    constexpr int kDSteps = D / 16;
+    constexpr int kDBlocks = D / 32;
+    static_assert(kChunks * kThreads == kTileQ * kUnits, "tile copy must split evenly");
+
+    __shared__ __attribute__((aligned(16))) char lds_a[kStageBytes];
+    __shared__ __attribute__((aligned(16))) char lds_b[kStageBytes];
+
+    const int tid = threadIdx.x;
+    const int wave = tid / 64;
+    const int lane = tid % 64;
+    const int l32 = lane % 32;
+    const int hi = lane / 32;
+
+    // ---- work partition: with a causal mask the first key blocks see the
+    // most queries, so they are launched first
+    const int BG = p.B * p.H_kv;
+    const int kblk = blockIdx.x / BG;
+    const int bg = blockIdx.x % BG;
+    const int b = bg / p.H_kv;
+    const int g = bg % p.H_kv;
+    const int L = p.L;
+    const int k_first = kblk * kBlockKV;
+    const int k_last = min(L, k_first + kBlockKV) - 1;
+
+    // ---- query range of the workgroup: rows that see at least one of its keys
+    int q_begin = 0, q_end = L;
+    if (CAUSAL) q_begin = k_first;
+    else if (WINDOW) q_begin = max(0, k_first - p.window);
+    if (WINDOW) q_end = min(L, k_last + p.window + 1);
+    const int tq_first = q_begin / kTileQ;
+    const int n_tq = (q_end + kTileQ - 1) / kTileQ - tq_first;
+    const int n_steps = p.group * n_tq;  // (head, query tile) pairs
+
+    // ---- this wave's keys; K and V fragments (B operands) in registers
+    const int ka = k_first + wave * kRowsPerWave;
+    const int kz = min(ka + kRowsPerWave, L) - 1;
+    const bool wave_live = ka < L;
+    const int kj = ka + l32;  // this lane's key column
+    const T *kh = static_cast<const T *>(p.k) + ((int64_t)b * p.H_kv + g) * L * D;
+    const T *vh = static_cast<const T *>(p.v) + ((int64_t)b * p.H_kv + g) * L * D;
+    vec8 kf[kDSteps], vf[kDSteps];
+#pragma unroll
+    for (int s = 0; s < kDSteps; ++s) {
+        if (kj < L) {
+            kf[s] = *reinterpret_cast<const vec8 *>(kh + (int64_t)kj * D + 16 * s + 8 * hi);
+            vf[s] = *reinterpret_cast<const vec8 *>(vh + (int64_t)kj * D + 16 * s + 8 * hi);
+        } else {
+            kf[s] = vec8{};
+            vf[s] = vec8{};
+        }
+    }
+    f32x16 acc_dk[kDBlocks], acc_dv[kDBlocks];
+#pragma unroll
+    for (int i = 0; i < kDBlocks; ++i) {
+        acc_dk[i] = f32x16{};
+        acc_dv[i] = f32x16{};
+    }
+
+    // ---- per-lane LDS byte offsets
+    const int qrow = k_row_for_lane(l32);
+    int roff[kDSteps];  // A operand rows (queries) of S = Q K^T and dP = dO V^T
+#pragma unroll
+    for (int ds = 0; ds < kDSteps; ++ds)
+        roff[ds] = qrow * kRowBytes + 16 * ((2 * ds + hi) ^ dual_swizzle<D>(qrow));
+    const int tr_row = 8 * hi + ((lane >> 2) & 3);
+    const int tr_unit = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    int troff[kDBlocks][2];  // transposing reads of dO^T and Q^T (rows +0 and +4)
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 2; ++r4) {
+            const int row = tr_row + 4 * r4;
+            troff[db][r4] = row * kRowBytes + 16 * ((4 * db + tr_unit) ^ dual_swizzle<D>(row)) + 8 * (lane & 1);
+        }
+    int ld_off[kChunks];  // source offsets of the tile copies (swizzled placement)
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+        const int unit_idx = (c * NW + wave) * 64 + lane;
+        const int row = unit_idx / kUnits, phys = unit_idx % kUnits;
+        ld_off[c] = row * kRowBytes + 16 * (phys ^ dual_swizzle<D>(row));
+    }
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+
+    // ---- global -> LDS copy of step n: the Q and dO tiles of (head, query
+    // tile) and the tile's workspace values; rows past L read as zeros
+    auto copy_step = [&](int n, char *stage) {
+        const int hh = n / n_tq;
+        const int q0 = (tq_first + n % n_tq) * kTileQ;
+        const int64_t bh = (int64_t)b * p.H + g * p.group + hh;
+        const int bytes = min(L - q0, kTileQ) * kRowBytes;
+        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(static_cast<const T *>(p.q) + (bh * L + q0) * D), 0, bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(static_cast<const T *>(p.dout) + (bh * L + q0) * D), 0, bytes, 0x00020000);
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+            const int region = (c * NW + wave_u) * 1024;
+            copy_to_lds16(rq, stage + region, ld_off[c]);
+            copy_to_lds16(rg, stage + kTileBytes + region, ld_off[c]);
+        }
+        if (wave_u == NW - 1) {
+            // lanes 0-15: -lse*log2e of the 64 rows, lanes 16-31: D, lanes
+            // 32-63: out of range (zeros into the spare half)
+            const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(p.ws + bh * 2 * p.Lp), 0, 2 * p.Lp * 4, 0x00020000);
+            const int off = lane < 16 ? 4 * (q0 + 4 * lane)
+                            : lane < 32 ? 4 * (p.Lp + q0 + 4 * (lane - 16)) : 8 * p.Lp;
+            copy_to_lds16(rw, stage + 2 * kTileBytes, off);
+        }
+    };
+
+    if (n_steps > 0) copy_step(0, lds_a);
+
+    auto process = [&](int n, char *cur, char *nxt) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
+        __syncthreads();
+        if (n + 1 < n_steps) copy_step(n + 1, nxt);
+
+        const int q0 = (tq_first + n % n_tq) * kTileQ;
+        const int q9 = q0 + kTileQ - 1;
+        bool skip = !wave_live;
+        if (CAUSAL) skip = skip || q9 < ka;
+        if (WINDOW) {
+            skip = skip || q0 - kz > p.window;
+            if (!CAUSAL) skip = skip || ka - q9 > p.window;
+        }
+        if (skip) return;
+        bool full = q9 < L;
+        if (CAUSAL) full = full && q0 >= kz;
+        if (WINDOW) {
+            full = full && q9 - ka <= p.window;
+            if (!CAUSAL) full = full && kz - q0 <= p.window;
+        }
+
+        const char *tq = cur;
+        const char *tg = cur + kTileBytes;
+        const float *tw = reinterpret_cast<const float *>(cur + 2 * kTileBytes);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys;
+            // register r of lane half hi holds query q0 + 32qb + 16(r/8) + 8hi + r%8
+            f32x16 s = f32x16{}, dp = f32x16{};
+            {
+                vec8 af[kDSteps], gf[kDSteps];
+#pragma unroll
+                for (int ds = 0; ds < kDSteps; ++ds) {
+                    af[ds] = *reinterpret_cast<const vec8 *>(tq + 32 * qb * kRowBytes + roff[ds]);
+                    gf[ds] = *reinterpret_cast<const vec8 *>(tg + 32 * qb * kRowBytes + roff[ds]);
+                }
+#pragma unroll
+                for (int ds = 0; ds < kDSteps; ++ds) s = mfma32(af[ds], kf[ds], s);
+#pragma unroll
+                for (int ds = 0; ds < kDSteps; ++ds) dp = mfma32(gf[ds], vf[ds], dp);
+            }
+            if (!full) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int i = q0 + 32 * qb + 16 * (r / 8) + 8 * hi + (r % 8);
+                    if (i >= L || !visible<CAUSAL, WINDOW>(i, kj, L, p.window)) s[r] = -INFINITY;
+                }
+            }
+            // P = exp2(s*scale*log2e - lse*log2e), dS = P (dP - D)
+            vec8 pv[2], dsv[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int base = 32 * qb + 16 * t + 8 * hi;  // first of this lane's 8 queries
+                f32x8 pf, df;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float lse2n = tw[base + e];
+                    const float dval = tw[kTileQ + base + e];
+                    pf[e] = __builtin_amdgcn_exp2f(fmaf(s[8 * t + e], p.scale_log2, lse2n));
+                    df[e] = pf[e] * (dp[8 * t + e] - dval);
+                }
+                pv[t] = __builtin_convertvector(pf, vec8);
+                dsv[t] = __builtin_convertvector(df, vec8);
+            }
+            // dV^T += dO^T P and dK^T += Q^T dS over the two 16-query slices
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int rbase = (32 * qb + 16 * t) * kRowBytes;
+#pragma unroll
+                for (int db = 0; db < kDBlocks; ++db) {
+                    const s16x4 g0 = lds_read_tr16(tg + rbase + troff[db][0]);
+                    const s16x4 g1 = lds_read_tr16(tg + rbase + troff[db][1]);
+                    const s16x4 q0v = lds_read_tr16(tq + rbase + troff[db][0]);
+                    const s16x4 q1v = lds_read_tr16(tq + rbase + troff[db][1]);
+                    const vec8 gt = __builtin_bit_cast(vec8, __builtin_shufflevector(g0, g1, 0, 1, 2, 3, 4, 5, 6, 7));
+                    const vec8 qt = __builtin_bit_cast(vec8, __builtin_shufflevector(q0v, q1v, 0, 1, 2, 3, 4, 5, 6, 7));
+                    acc_dv[db] = mfma32(gt, pv[t], acc_dv[db]);
+                    acc_dk[db] = mfma32(qt, dsv[t], acc_dk[db]);
+                }
+            }
+        }
+    };
+
+    for (int n = 0; n < n_steps; n += 2) {
+        process(n, lds_a, lds_b);
+        if (n + 1 < n_steps) process(n + 1, lds_b, lds_a);
+    }
+
+    // ---- epilogue: register 4a+c of block db holds d = 32db + 8a + 4hi + c
+    // of key kj
+    if (!wave_live || kj >= L) return;
+    T *dkrow = static_cast<T *>(p.dk) + (((int64_t)b * p.H_kv + g) * L + kj) * D;
+    T *dvrow = static_cast<T *>(p.dv) + (((int64_t)b * p.H_kv + g) * L + kj) * D;
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            T kv4[4], vv4[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                kv4[c] = (T)(acc_dk[db][4 * a + c] * p.scale);
+                vv4[c] = (T)acc_dv[db][4 * a + c];
+            }
+            *reinterpret_cast<uint64_t *>(dkrow + 32 * db + 8 * a + 4 * hi) = *reinterpret_cast<const uint64_t *>(kv4);
+            *reinterpret_cast<uint64_t *>(dvrow + 32 * db + 8 * a + 4 * hi) = *reinterpret_cast<const uint64_t *>(vv4);
+        }
+}
+
+// ---------------------------------------------------------------- 3. dQ
+template <typename T, int D, bool CAUSAL, bool WINDOW, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_bwd_dq_kernel(BwdParams p)
+{
+    typedef typename Vec8<T>::type vec8;
+    constexpr int kThreads = 64 * NW;
+    constexpr int kBlockQ = kRowsPerWave * NW;
+    constexpr int kRowBytes = 2 * D;
+    constexpr int kTileBytes = kBlockK * kRowBytes;       // one K or V tile
+    constexpr int kUnits = D / 8;
+    constexpr int kChunks = kBlockK * kUnits / kThreads;
+    constexpr int kDSteps = D / 16;
+    constexpr int kDBlocks = D / 32;
+    static_assert(kChunks * kThreads == kBlockK * kUnits, "tile copy must split evenly");
+
+    // two stages of [K | V] tiles, as separate objects
+    __shared__ __attribute__((aligned(16))) char lds_a[2][kTileBytes];
+    __shared__ __attribute__((aligned(16))) char lds_b[2][kTileBytes];
+
+    const int tid = threadIdx.x;
+    const int wave = tid / 64;
+    const int lane = tid % 64;
+    const int l32 = lane % 32;
+    const int hi = lane / 32;
+
+    // ---- work partition: heaviest query blocks first when causal
+    const int BH = p.B * p.H;
+    const int order = blockIdx.x / BH;
+    const int bh = blockIdx.x % BH;
+    const int qblk = CAUSAL ? (p.n_blk - 1 - order) : order;
+    const int b = bh / p.H;
+    const int h = bh % p.H;
+    const int g = h / p.group;
+    const int L = p.L;
+
+    const T *qh = static_cast<const T *>(p.q) + ((int64_t)b * p.H + h) * L * D;
+    const T *gh = static_cast<const T *>(p.dout) + ((int64_t)b * p.H + h) * L * D;
+    const T *kh = static_cast<const T *>(p.k) + ((int64_t)b * p.H_kv + g) * L * D;
+    const T *vh = static_cast<const T *>(p.v) + ((int64_t)b * p.H_kv + g) * L * D;
+    const float *wsh = p.ws + (int64_t)bh * 2 * p.Lp;
+
+    // ---- key range of the workgroup
+    const int q_first = qblk * kBlockQ;
+    const int q_last = min(L, q_first + kBlockQ) - 1;
+    int kv_begin = 0, kv_end = L;
+    if (WINDOW) kv_begin = max(0, q_first - p.window);
+    if (CAUSAL) kv_end = q_last + 1;
+    else if (WINDOW) kv_end = min(L, q_last + p.window + 1);
+    const int t_first = kv_begin / kBlockK;
+    const int t_last = (kv_end + kBlockK - 1) / kBlockK;
+
+    // ---- this wave's query rows; Q^T and dO^T fragments in registers
+    const int qa = q_first + wave * kRowsPerWave;
+    const int qz = min(qa + kRowsPerWave, L) - 1;
+    const bool wave_live = qa < L;
+    const int qi = qa + l32;
+    vec8 qf[kDSteps], gf[kDSteps];
+#pragma unroll
+    for (int s = 0; s < kDSteps; ++s) {
+        if (qi < L) {
+            qf[s] = *reinterpret_cast<const vec8 *>(qh + (int64_t)qi * D + 16 * s + 8 * hi);
+            gf[s] = *reinterpret_cast<const vec8 *>(gh + (int64_t)qi * D + 16 * s + 8 * hi);
+        } else {
+            qf[s] = vec8{};
+            gf[s] = vec8{};
+        }
+    }
+    const float lse2n = qi < L ? wsh[qi] : 0.f;
+    const float dval = qi < L ? wsh[p.Lp + qi] : 0.f;
+    f32x16 acc_dq[kDBlocks];
+#pragma unroll
+    for (int i = 0; i < kDBlocks; ++i) acc_dq[i] = f32x16{};
+
+    // ---- per-lane LDS byte offsets: K is read both by rows and transposed
+    // (dual swizzle), V only by rows (K swizzle)
+    const int krow = k_row_for_lane(l32);
+    int koff[kDSteps], voff[kDSteps];
+#pragma unroll
+    for (int ds = 0; ds < kDSteps; ++ds) {
+        koff[ds] = krow * kRowBytes + 16 * ((2 * ds + hi) ^ dual_swizzle<D>(krow));
+        voff[ds] = krow * kRowBytes + 16 * ((2 * ds + hi) ^ k_swizzle<D>(krow));
+    }
+    const int tr_row = 8 * hi + ((lane >> 2) & 3);
+    const int tr_unit = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    int ktr[kDBlocks][2];
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 2; ++r4) {
+            const int row = tr_row + 4 * r4;
+            ktr[db][r4] = row * kRowBytes + 16 * ((4 * db + tr_unit) ^ dual_swizzle<D>(row)) + 8 * (lane & 1);
+        }
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    int ld_k[kChunks], ld_v[kChunks];
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+        const int unit_idx = (c * NW + wave) * 64 + lane;
+        const int row = unit_idx / kUnits, phys = unit_idx % kUnits;
+        ld_k[c] = row * kRowBytes + 16 * (phys ^ dual_swizzle<D>(row));
+        ld_v[c] = row * kRowBytes + 16 * (phys ^ k_swizzle<D>(row));
+    }
+    auto copy_tile = [&](int t, char (*stage)[kTileBytes]) {
+        const int j0 = t * kBlockK;
+        const int bytes = min(L - j0, kBlockK) * kRowBytes;
+        const __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(kh + (int64_t)j0 * D), 0, bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(vh + (int64_t)j0 * D), 0, bytes, 0x00020000);
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+            const int region = (c * NW + wave_u) * 1024;
+            copy_to_lds16(rk, &stage[0][region], ld_k[c]);
+            copy_to_lds16(rv, &stage[1][region], ld_v[c]);
+        }
+    };
+
+    if (t_first < t_last) copy_tile(t_first, lds_a);
+
+    auto process = [&](int t, char (*cur)[kTileBytes], char (*nxt)[kTileBytes]) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __syncthreads();
+        if (t + 1 < t_last) copy_tile(t + 1, nxt);
+
+        const int j0 = t * kBlockK;
+        const int j_last = j0 + kBlockK - 1;
+        bool skip = !wave_live;
+        if (CAUSAL) skip = skip || j0 > qz;
+        if (WINDOW) {
+            skip = skip || j_last < qa - p.window;
+            if (!CAUSAL) skip = skip || j0 > qz + p.window;
+        }
+        if (skip) return;
+        bool full = j_last < L;
+        if (CAUSAL) full = full && j_last <= qa;
+        if (WINDOW) {
+            full = full && j0 >= qz - p.window;
+            if (!CAUSAL) full = full && j_last <= qa + p.window;
+        }
+
+        const char *tk = cur[0];
+        const char *tv = cur[1];
+        // S^T = K Q^T and dP^T = V dO^T; register r of block kb holds key
+        // j0 + 32kb + 16(r/8) + 8hi + r%8 of query qi
+        f32x16 s[2], dp[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            vec8 af[kDSteps], bf[kDSteps];
+#pragma unroll
+            for (int ds = 0; ds < kDSteps; ++ds) {
+                af[ds] = *reinterpret_cast<const vec8 *>(tk + 32 * kb * kRowBytes + koff[ds]);
+                bf[ds] = *reinterpret_cast<const vec8 *>(tv + 32 * kb * kRowBytes + voff[ds]);
+            }
+            s[kb] = f32x16{};
+            dp[kb] = f32x16{};
+#pragma unroll
+            for (int ds = 0; ds < kDSteps; ++ds) s[kb] = mfma32(af[ds], qf[ds], s[kb]);
+#pragma unroll
+            for (int ds = 0; ds < kDSteps; ++ds) dp[kb] = mfma32(bf[ds], gf[ds], dp[kb]);
+        }
+        if (!full) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int j = j0 + 32 * kb + 16 * (r / 8) + 8 * hi + (r % 8);
+                    if (!visible<CAUSAL, WINDOW>(qi, j, L, p.window)) s[kb][r] = -INFINITY;
+                }
+        }
+        // dS^T, rounded: the B operand of dQ^T += K^T dS^T, 16 keys per slice
+        vec8 dsv[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            f32x8 df;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float pe = __builtin_amdgcn_exp2f(fmaf(s[ks / 2][8 * (ks % 2) + e], p.scale_log2, lse2n));
+                df[e] = pe * (dp[ks / 2][8 * (ks % 2) + e] - dval);
+            }
+            dsv[ks] = __builtin_convertvector(df, vec8);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int db = 0; db < kDBlocks; ++db) {
+                const char *base = tk + 16 * ks * kRowBytes;
+                const s16x4 lo4 = lds_read_tr16(base + ktr[db][0]);
+                const s16x4 hi4 = lds_read_tr16(base + ktr[db][1]);
+                const vec8 kt = __builtin_bit_cast(vec8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+                acc_dq[db] = mfma32(kt, dsv[ks], acc_dq[db]);
+            }
+    };
+
+    for (int t = t_first; t < t_last; t += 2) {
+        process(t, lds_a, lds_b);
+        if (t + 1 < t_last) process(t + 1, lds_b, lds_a);
+    }
+
+    // ---- epilogue: register 4a+c of block db holds d = 32db + 8a + 4hi + c
+    if (!wave_live || qi >= L) return;
+    T *dqrow = static_cast<T *>(p.dq) + (((int64_t)b * p.H + h) * L + qi) * D;
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            T outv[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) outv[c] = (T)(acc_dq[db][4 * a + c] * p.scale);
+            *reinterpret_cast<uint64_t *>(dqrow + 32 * db + 8 * a + 4 * hi) = *reinterpret_cast<const uint64_t *>(outv);
+        }
+}
+
+// ------------------------------------------------------------------ host side
+
+constexpr int kBwdWaves = 4;  // waves per workgroup of both gradient kernels
+
+template <typename T, int D, bool CAUSAL, bool WINDOW>
+hipError_t launch_bwd_instance(BwdParams p, hipStream_t stream)
+{
+    constexpr int NW = kBwdWaves;
+    constexpr int kRows = kRowsPerWave * NW;
+    void *kargs[] = {&p};
+    p.n_blk = (p.L + kRows - 1) / kRows;
+    hipError_t err = hipLaunchKernel(reinterpret_cast<const void *>(&attn_bwd_dkdv_kernel<T, D, CAUSAL, WINDOW, NW>),
+                                     dim3((unsigned)((int64_t)p.n_blk * p.B * p.H_kv)), dim3(64 * NW), kargs, 0,
+                                     stream);
+    if (err != hipSuccess) return err;
+    return hipLaunchKernel(reinterpret_cast<const void *>(&attn_bwd_dq_kernel<T, D, CAUSAL, WINDOW, NW>),
+                           dim3((unsigned)((int64_t)p.n_blk * p.B * p.H)), dim3(64 * NW), kargs, 0, stream);
+}
+
+template <typename T, int D>
+hipError_t launch_bwd(BwdParams p, bool causal, bool window, hipStream_t stream)
+{
+    {
+        constexpr int kRowsPerBlock = 256 / (D / 8);
+        const int64_t rows = (int64_t)p.B * p.H * p.Lp;
+        void *kargs[] = {&p};
+        const hipError_t err = hipLaunchKernel(reinterpret_cast<const void *>(&attn_bwd_prep_kernel<T, D>),
+                                               dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)),
+                                               dim3(256), kargs, 0, stream);
+        if (err != hipSuccess) return err;
+    }
+    if (causal)
+        return window ? launch_bwd_instance<T, D, true, true>(p, stream)
+                      : launch_bwd_instance<T, D, true, false>(p, stream);
+    return window ? launch_bwd_instance<T, D, false, true>(p, stream)
+                  : launch_bwd_instance<T, D, false, false>(p, stream);
+}
+
+int64_t padded_len(int64_t L) { return (L + kTileQ - 1) / kTileQ * kTileQ; }
+
+template <typename T>
+int attn_backward(const void *q, const void *k, const void *v, const void *out, const void *dout,
+                  const float *lse, void *dq, void *dk, void *dv, void *workspace, int B, int H, int H_kv,
+                  int L, int d, int causal, int window, float scale, void *stream)
+{
+    if (B < 0 || L < 0 || H < 1 || H_kv < 1 || H % H_kv != 0) return ATTN_ERR_SHAPE;
+    if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+    if (window < -1) return ATTN_ERR_WINDOW;
+    if (causal != 0 && causal != 1) return ATTN_ERR_FLAG;
+    if (std::isinf(scale)) return ATTN_ERR_SCALE;
+    if (B == 0 || L == 0) return ATTN_OK;
+    if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !workspace) return ATTN_ERR_NULL;
+    const uintptr_t a16 = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                          reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(out) |
+                          reinterpret_cast<uintptr_t>(dout) | reinterpret_cast<uintptr_t>(dq) |
+                          reinterpret_cast<uintptr_t>(dk) | reinterpret_cast<uintptr_t>(dv) |
+                          reinterpret_cast<uintptr_t>(workspace);
+    if ((a16 & 15) || (reinterpret_cast<uintptr_t>(lse) & 3)) return ATTN_ERR_ALIGN;
+
+    const unsigned __int128 rows_q = (unsigned __int128)B * H * L;
+    const unsigned __int128 rows_kv = (unsigned __int128)B * H_kv * L;
+    if (rows_q * d * sizeof(T) >= ((unsigned __int128)1 << 62)) return ATTN_ERR_SIZE;
+    const int64_t Lp = padded_len(L);
+    const size_t bytes_q = (size_t)(rows_q * d * sizeof(T));
+    const size_t bytes_kv = (size_t)(rows_kv * d * sizeof(T));
+    const size_t bytes_lse = (size_t)(rows_q * sizeof(float));
+    const size_t bytes_ws = (size_t)B * H * Lp * 2 * sizeof(float);
+    // grid sizes (the prep grid is the largest) and the workspace offsets
+    // (32-bit buffer ranges: 2*Lp floats per head)
+    if ((int64_t)B * H * Lp / 16 > INT_MAX || 8 * Lp > INT_MAX) return ATTN_ERR_SIZE;
+
+    const void *ins[] = {q, k, v, out, dout, lse};
+    const size_t in_bytes[] = {bytes_q, bytes_kv, bytes_kv, bytes_q, bytes_q, bytes_lse};
+    const void *outs[] = {dq, dk, dv, workspace};
+    const size_t out_bytes[] = {bytes_q, bytes_kv, bytes_kv, bytes_ws};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return ATTN_ERR_ALIAS;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return ATTN_ERR_ALIAS;
+    }
+
+    BwdParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.o = out;
+    p.dout = dout;
+    p.lse = lse;
+    p.ws = static_cast<float *>(workspace);
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.B = B;
+    p.H = H;
+    p.H_kv = H_kv;
+    p.L = L;
+    p.Lp = (int)Lp;
+    p.group = H / H_kv;
+    p.window = window;
+    p.n_blk = 0;
+    p.scale = attn_resolve_scale(scale, d);
+    p.scale_log2 = p.scale * kLog2e;
+
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool win = window >= 0;
+    const hipError_t err = d == 64 ? launch_bwd<T, 64>(p, causal, win, s) : launch_bwd<T, 128>(p, causal, win, s);
+    return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_bwd_workspace_size(int B, int H, int L)
+{
+    if (B <= 0 || H <= 0 || L <= 0) return 0;
+    return (size_t)B * (size_t)H * (size_t)padded_len(L) * 2 * sizeof(float);
+}
+
+int attn_bwd(const void *q, const void *k, const void *v, const void *out, const void *dout, const float *lse,
+             void *dq, void *dk, void *dv, void *workspace, int B, int H, int H_kv, int L, int d, int causal,
+             int window, float scale, void *stream)
+{
+    return attn_backward<_Float16>(q, k, v, out, dout, lse, dq, dk, dv, workspace, B, H, H_kv, L, d, causal,
+                                   window, scale, stream);
+}
+
+int attn_bwd_bf16(const void *q, const void *k, const void *v, const void *out, const void *dout,
+                  const float *lse, void *dq, void *dk, void *dv, void *workspace, int B, int H, int H_kv, int L,
+                  int d, int causal, int window, float scale, void *stream)
+{
+    return attn_backward<__bf16>(q, k, v, out, dout, lse, dq, dk, dv, workspace, B, H, H_kv, L, d, causal,
+                                 window, scale, stream);
+}
+
+}  // extern "C"

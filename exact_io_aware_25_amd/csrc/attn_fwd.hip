@@ -12,8 +12,11 @@
 //
 // The pages' own kernels target NVIDIA parts (shared-memory tiling, TMA,
 // warp groups).  This file is written for gfx950:
-//   * one workgroup = 4 waves of 64 lanes = 128 query rows of one (b, h);
-//     each wave owns 32 query rows for the whole pass;
+//   * a key-range group = 4 or 8 waves of 64 lanes = 128 or 256 query rows of
+//     one (b, h); each wave owns 32 query rows for the whole pass; a
+//     workgroup holds 1, 2 or 4 groups that split the key range and merge
+//     their partial results exactly at the end (the launch shape is chosen
+//     per problem, see launch_shape);
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_{f16,bf16} with K as the A operand
 //     and Q^T (kept in registers) as the B operand.  In the 32x32 accumulator
 //     layout a lane then holds 16 keys of ONE query, so the softmax row
@@ -22,10 +25,11 @@
 //   * the K rows feeding the A operand are permuted (bits 2 and 3 of the row
 //     index swapped) so that the fp32 score registers, rounded to 16 bits,
 //     are directly the B operand (P^T) of the second product O^T = V^T P^T;
-//   * V is written to LDS transposed (V^T, keys contiguous) so the A operand
-//     of O^T = V^T P^T is one 16-byte LDS read per lane;
-//   * K and V tiles are double-buffered in LDS: global loads of tile t+1 are
-//     in flight while tile t is multiplied;
+//   * V stays row-major in LDS and the A operand V^T of the second product
+//     comes from transposing LDS reads (ds_read_b64_tr_b16);
+//   * K and V tiles go from device memory straight into LDS (buffer loads
+//     with an LDS destination), double-buffered: the copy of tile t+1 is in
+//     flight while tile t is multiplied;
 //   * the softmax runs in the exp2 domain with scale*log2(e) folded in, and
 //     O^T stays in fp32 accumulators until a single final write.
 #include <hip/hip_runtime.h>
@@ -36,30 +40,9 @@
 #include <type_traits>
 
 #include "attn.h"
+#include "attn_common.h"
 
 namespace {
-
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kRowsPerWave = 32;
-constexpr int kBlockK = 64;  // keys per K/V tile
-
-template <typename T> struct Vec8;
-template <> struct Vec8<_Float16> { typedef f16x8 type; };
-template <> struct Vec8<__bf16> { typedef bf16x8 type; };
-
-__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c)
-{
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
-{
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 
 struct Params {
     const void *q, *k, *v;
@@ -71,91 +54,6 @@ struct Params {
     int n_qblk;         // ceil(L / kBlockQ)
     float scale_log2;   // scale * log2(e)
 };
-
-// Row of the K tile that feeds A-operand row m: bits 2 and 3 swapped.  With
-// this order, accumulator register r (0..15) of lane half `hi` in a 32-key
-// block holds key 16*(r/8) + 8*hi + r%8, i.e. 8 consecutive keys per 16-key
-// slice -- the layout the B operand of the second product needs.
-__device__ __forceinline__ int k_row_for_lane(int m)
-{
-    return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1);
-}
-
-template <bool CAUSAL, bool WINDOW>
-__device__ __forceinline__ bool visible(int i, int j, int L, int window)
-{
-    if (j >= L) return false;
-    if (CAUSAL && j > i) return false;
-    if (WINDOW) {
-        if (i - j > window) return false;
-        if (!CAUSAL && j - i > window) return false;
-    }
-    return true;
-}
-
-// XOR swizzles of the 16-byte units of each LDS tile row (tiles are not
-// padded).  A row of D 16-bit values has D/8 units; unit u of row r is stored
-// at unit u ^ f(r).  The functions are chosen so that both reads are free of
-// bank conflicts whether the LDS serves 8 lanes x 16 bytes (32 banks) or 16
-// lanes x 16 bytes (64 banks) per cycle:
-//  * K is read 16 bytes per lane from the 16 rows k_row_for_lane(0..15) of a
-//    32-row block, all at the same logical unit: f must be a bijection on row
-//    bits {0,1,3} (the first 8 of those rows) and on bits {1,2,3} for a fixed
-//    bit 0 (16 rows over two 128-byte halves);
-//  * V is read 8 bytes per lane by the transposing load, four consecutive rows
-//    at a time with two (16 lanes) or four (32 lanes) consecutive units per
-//    row: f must move the unit pair, and for 32 lanes the unit quad, of each
-//    of the four rows to a different place.
-template <int D> __device__ __forceinline__ int k_swizzle(int row)
-{
-    const int b0 = row & 1, b1 = (row >> 1) & 1, b2 = (row >> 2) & 1, b3 = (row >> 3) & 1;
-    return (b0 ^ b2) | (b1 << 1) | (b3 << 2) | (D == 128 ? (b2 << 3) : 0);
-}
-template <int D> __device__ __forceinline__ int v_swizzle(int row)
-{
-    const int c = row & 3;
-    return (c << 1) | (D == 128 ? ((c & 1) << 3) : 0);
-}
-
-// Copy 16 bytes per lane from a buffer into LDS without passing through
-// VGPRs: lane i's bytes land at lds_dst + 16*i (lds_dst is wave-uniform).
-__device__ __forceinline__ void copy_to_lds16(__amdgpu_buffer_rsrc_t src, void *lds_dst, int src_offset)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void *)lds_dst, 16,
-                                             src_offset, 0, 0, 0);
-}
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// Transposing 8-byte LDS read: within each group of 16 lanes, lane 4a+b gets
-// element b of the 8-byte chunks addressed by lanes a, a+4, a+8 and a+12.
-__device__ __forceinline__ s16x4 lds_read_tr16(const void *generic_lds_ptr)
-{
-    auto p = (__attribute__((address_space(3))) char *)(generic_lds_ptr);
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p);
-}
-
-__device__ __forceinline__ float half_swap_max(float x)
-{
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float half_swap_sum(float x)
-{
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ float sum8(f16x8 v, float acc)
-{
-    const f16x2 one = {1, 1};
-    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
-    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
-    acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
-    return __builtin_amdgcn_fdot2(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
-}
 
 // Largest per-lane tile sum of softmax weights the fast path accepts.  It
 // bounds every weight by 2^15, inside fp16 range, and keeps the sum of a
@@ -498,12 +396,6 @@ __global__ __launch_bounds__(64 * NW * SPLIT) void attn_fwd_kernel(Params p)
 
 // ------------------------------------------------------------------ host side
 
-bool overlaps(const void *a, size_t na, const void *b, size_t nb)
-{
-    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
-    return na && nb && pa < pb + nb && pb < pa + na;
-}
-
 template <typename T, int D, bool CAUSAL, bool WINDOW, int NW, int SPLIT>
 hipError_t launch_waves(Params p, hipStream_t stream)
 {
@@ -662,12 +554,12 @@ const char *attn_status_string(int status)
     case ATTN_ERR_SHAPE: return "bad shape: need B >= 0, L >= 0, H >= 1, H_kv >= 1, H % H_kv == 0";
     case ATTN_ERR_HEAD_DIM: return "head dimension must be 64 or 128";
     case ATTN_ERR_WINDOW: return "window must be -1 (none) or >= 0";
-    case ATTN_ERR_ALIAS: return "out or lse overlaps another tensor";
+    case ATTN_ERR_ALIAS: return "an output overlaps another tensor";
     case ATTN_ERR_LAUNCH: return "kernel launch failed";
     case ATTN_ERR_SIZE: return "problem too large to index";
     case ATTN_ERR_FLAG: return "causal must be 0 or 1";
     case ATTN_ERR_SCALE: return "scale must be finite";
-    case ATTN_ERR_ALIGN: return "q, k, v, out must be 16-byte aligned and lse 4-byte aligned";
+    case ATTN_ERR_ALIGN: return "tensors must be 16-byte aligned (lse 4-byte aligned)";
     default: return "unknown status";
     }
 }

@@ -1,5 +1,6 @@
 /*
- * attn.h -- C ABI of the exact attention forward pass for AMD MI355X (gfx950).
+ * attn.h -- C ABI of exact attention (forward and backward passes) for AMD
+ * MI355X (gfx950).
  *
  * The operation is exact scaled-dot-product attention computed the
  * IO-aware way: Q, K and V are streamed through on-chip tiles, the softmax is
@@ -37,8 +38,7 @@
  * Ownership and behaviour:
  *   - Every tensor pointer is a DEVICE pointer owned by the caller, who
  *     allocates and frees it.  The library allocates no device memory, keeps
- *     no state between calls except a once-filled table of device properties,
- *     and never synchronises.
+ *     no state between calls, and never synchronises.
  *   - stream is a hipStream_t (NULL = the default stream).  The call enqueues
  *     the kernel on it and returns; results are ready once the stream has
  *     reached that point.  Calls on different streams may run concurrently.
@@ -57,6 +57,8 @@
 #ifndef EXACT_IO_AWARE_ATTN_H
 #define EXACT_IO_AWARE_ATTN_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -68,12 +70,12 @@ enum attn_status {
     ATTN_ERR_SHAPE = 2,    /* B < 0, L < 0, H < 1, H_kv < 1, or H not a multiple of H_kv   */
     ATTN_ERR_HEAD_DIM = 3, /* d is neither 64 nor 128                                       */
     ATTN_ERR_WINDOW = 4,   /* window < -1                                                   */
-    ATTN_ERR_ALIAS = 5,    /* out or lse overlaps another tensor                            */
+    ATTN_ERR_ALIAS = 5,    /* an output overlaps another tensor                             */
     ATTN_ERR_LAUNCH = 6,   /* the HIP runtime refused the launch (no gfx950 device, ...)    */
     ATTN_ERR_SIZE = 7,     /* a tensor or the grid is too large to index                    */
     ATTN_ERR_FLAG = 8,     /* causal is neither 0 nor 1                                     */
     ATTN_ERR_SCALE = 9,    /* scale is +/- infinity                                         */
-    ATTN_ERR_ALIGN = 10    /* q, k, v or out not 16-byte aligned, or lse not 4-byte aligned */
+    ATTN_ERR_ALIGN = 10    /* a tensor not 16-byte aligned, or lse not 4-byte aligned        */
 };
 
 /*
@@ -101,6 +103,51 @@ const char *attn_status_string(int status);
  * for attn_fwd; H_kv plays no part). */
 int attn_launch_shape(int B, int H, int L, int d, int causal, int window, int *waves_per_group,
                       int *key_splits);
+
+/*
+ * Backward pass: the gradients of the forward above with respect to q, k and
+ * v, for an upstream gradient dout of out.  The pages recommend the method
+ * for training («Оптимизация внимания Flash», introduction) and name the
+ * backward pass as the part their benchmark left unmeasured («ТЕХНИЧЕСКОЕ
+ * ЗАДАНИЕ: Сравнить Hyena vs FlashAttention на 128k», stage 5); it is the
+ * gradient of the definition above, computed the same IO-aware way (softmax
+ * weights recomputed tile by tile from lse, nothing L x L in memory).  With
+ * P_ij = exp(scale q_i . k_j - lse_i) for j in V(i):
+ *
+ *   D_i   = dout_i . out_i
+ *   dS_ij = P_ij (dout_i . v_j - D_i)
+ *   dq_i  = scale * sum_j dS_ij k_j
+ *   dk_j  = scale * sum_i dS_ij q_i          (i over every row of every query
+ *   dv_j  = sum_i P_ij dout_i                 head that reads k_j's K/V head)
+ *
+ * Inputs: q, k, v, causal, window, scale exactly as given to the forward
+ * call, out and lse as it wrote them, dout [B, H, L, d] (same 16-bit type).
+ * Outputs (overwritten): dq [B, H, L, d], dk and dv [B, H_kv, L, d], same
+ * 16-bit type, each element rounded once from an fp32 accumulator.
+ * workspace: caller-owned device memory of attn_bwd_workspace_size(B, H, L)
+ * bytes, 16-byte aligned; on return it holds, per (b, h), Lp values of
+ * -lse*log2(e) followed by Lp values of D (Lp = L rounded up to a multiple of
+ * 64; the padding rows hold zeros), in fp32.
+ * Behaviour as for attn_fwd: device pointers, enqueue on `stream` and return,
+ * no allocation, no synchronisation, arguments checked before any HIP call,
+ * B = 0 or L = 0 is an empty problem.  dq, dk, dv and workspace must not
+ * overlap one another or any input; every pointer except lse (4 bytes) must
+ * be 16-byte aligned.  The result is deterministic (no atomics).
+ */
+int attn_bwd(const void *q, const void *k, const void *v, const void *out, const void *dout,
+             const float *lse, void *dq, void *dk, void *dv, void *workspace,
+             int B, int H, int H_kv, int L, int d, int causal, int window, float scale,
+             void *stream);
+
+/* The same backward pass for bfloat16 tensors (lse and workspace stay fp32). */
+int attn_bwd_bf16(const void *q, const void *k, const void *v, const void *out, const void *dout,
+                  const float *lse, void *dq, void *dk, void *dv, void *workspace,
+                  int B, int H, int H_kv, int L, int d, int causal, int window, float scale,
+                  void *stream);
+
+/* Bytes of workspace attn_bwd / attn_bwd_bf16 need for B, H, L
+ * (8 * B * H * Lp); 0 if any of them is <= 0.  Host-only. */
+size_t attn_bwd_workspace_size(int B, int H, int L);
 
 /* The fp32 scale the kernels use for a given scale argument and head size:
  * `scale` itself when finite and > 0, else the fp32 value nearest 1/sqrt(d).

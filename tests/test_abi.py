@@ -90,8 +90,9 @@ def test_binding_does_not_import_the_oracle():
     import sys
     src = open(os.path.join(ROOT, "exact_io_aware_25_amd", "__init__.py")).read()
     assert "oracle" not in src.replace("no fallback", "")
-    hip = open(os.path.join(ROOT, "exact_io_aware_25_amd", "csrc", "attn_fwd.hip")).read()
-    assert "oracle" not in hip
+    for name in ("attn_fwd.hip", "attn_bwd.hip", "attn_common.h"):
+        hip = open(os.path.join(ROOT, "exact_io_aware_25_amd", "csrc", name)).read()
+        assert "oracle" not in hip, name
 
 
 def test_launch_shape():
@@ -117,3 +118,57 @@ def test_launch_shape():
         shape(1, 4, 100, 96, True, -1)
     with pytest.raises(ValueError):
         shape(1, 4, 100, 64, 2, -1)
+
+
+# fake addresses for the backward's extra tensors, beyond the forward's
+DO, DQ, DK, DV, WS = (0x10000000 + i * (1 << 20) for i in range(5, 10))
+
+
+def call_bwd(fn=attn.attn_bwd, q=Q, k=K, v=V, o=O, do=DO, lse=LSE, dq=DQ, dk=DK, dv=DV, ws=WS, B=1, H=4,
+             H_kv=2, L=256, d=64, causal=1, window=-1, scale=0.125):
+    return fn(q, k, v, o, do, lse, dq, dk, dv, ws, B, H, H_kv, L, d, causal, window, scale, None)
+
+
+@pytest.mark.parametrize("fn", [attn.attn_bwd, attn.attn_bwd_bf16])
+def test_backward_argument_errors(fn):
+    for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "ws"):
+        assert call_bwd(fn, **{name: 0}) == attn.ATTN_ERR_NULL, name
+    assert call_bwd(fn, H=3, H_kv=2) == attn.ATTN_ERR_SHAPE
+    assert call_bwd(fn, H_kv=0) == attn.ATTN_ERR_SHAPE
+    assert call_bwd(fn, B=-1) == attn.ATTN_ERR_SHAPE
+    assert call_bwd(fn, L=-1) == attn.ATTN_ERR_SHAPE
+    for d in (0, 32, 96, 256):
+        assert call_bwd(fn, d=d) == attn.ATTN_ERR_HEAD_DIM
+    assert call_bwd(fn, window=-3) == attn.ATTN_ERR_WINDOW
+    assert call_bwd(fn, causal=3) == attn.ATTN_ERR_FLAG
+    assert call_bwd(fn, scale=float("inf")) == attn.ATTN_ERR_SCALE
+    # outputs must not overlap inputs or one another
+    assert call_bwd(fn, dq=Q) == attn.ATTN_ERR_ALIAS
+    assert call_bwd(fn, dk=DO + 4096) == attn.ATTN_ERR_ALIAS
+    assert call_bwd(fn, dv=LSE) == attn.ATTN_ERR_ALIAS
+    assert call_bwd(fn, ws=DQ + 16) == attn.ATTN_ERR_ALIAS
+    assert call_bwd(fn, dk=DV) == attn.ATTN_ERR_ALIAS
+    assert call_bwd(fn, ws=O) == attn.ATTN_ERR_ALIAS
+    # inputs may overlap one another (they are only read)
+    assert call_bwd(fn, do=O, k=V, B=0) == attn.ATTN_OK
+    for name in ("q", "k", "v", "o", "do", "dq", "dk", "dv", "ws"):
+        assert call_bwd(fn, **{name: globals()[{"o": "O", "do": "DO", "ws": "WS"}.get(name, name.upper())] + 8}) \
+            == attn.ATTN_ERR_ALIGN, name
+    assert call_bwd(fn, lse=LSE + 2) == attn.ATTN_ERR_ALIGN
+    assert call_bwd(fn, L=1 << 30, H=1 << 12, H_kv=1) == attn.ATTN_ERR_SIZE
+
+
+@pytest.mark.parametrize("fn", [attn.attn_bwd, attn.attn_bwd_bf16])
+def test_backward_empty_problems(fn):
+    z = dict(q=0, k=0, v=0, o=0, do=0, lse=0, dq=0, dk=0, dv=0, ws=0)
+    assert call_bwd(fn, B=0, **z) == attn.ATTN_OK
+    assert call_bwd(fn, L=0, **z) == attn.ATTN_OK
+
+
+def test_backward_workspace_size():
+    assert attn.attn_bwd_workspace_size(1, 4, 256) == 1 * 4 * 256 * 8
+    assert attn.attn_bwd_workspace_size(2, 3, 65) == 2 * 3 * 128 * 8      # rows padded to 64
+    assert attn.attn_bwd_workspace_size(1, 1, 1) == 64 * 8
+    assert attn.attn_bwd_workspace_size(0, 4, 256) == 0
+    assert attn.attn_bwd_workspace_size(1, 4, 0) == 0
+    assert attn.attn_bwd_workspace_size(1, -1, 5) == 0

@@ -10,6 +10,13 @@ the fp64 oracle timed on a bounded sample of the same workload's rows (whose
 GPU outputs are also checked against it).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--sweep]
+    python bench.py --backward [...]
+
+With --backward, one step is one attn_bwd call (dq, dk, dv for an upstream
+gradient, from the forward's out and lse) on the same workload, and the line
+reports the backward's throughput: algorithmic FLOPs 10*d per visible pair
+(the five products of the backward: scores recomputed, dP, dV, dK, dQ), i.e.
+2.5 times the forward's.
 """
 from __future__ import annotations
 
@@ -31,6 +38,7 @@ from synth import WORKLOADS, workload_inputs  # noqa: E402
 MFMA_PEAK_F16_TFLOPS = 2516.6   # MI355X dense fp16/bf16: 256 CU x 4096 FLOP/clk x 2.4 GHz
 HBM_PEAK_GBS = 8000.0
 METRIC = "causal attn fwd TFLOP/s @ L=128k,H=4,d=64 fp16; % of MFMA peak"
+METRIC_BWD = "causal attn bwd TFLOP/s @ L=128k,H=4,d=64 fp16; % of MFMA peak"
 DEFAULT_WORKLOAD = "causal_128k_h4"
 
 
@@ -56,6 +64,17 @@ def row_visible(i: np.ndarray, L: int, causal: bool, window: int) -> np.ndarray:
 
 def algorithmic_flops(w) -> float:
     return 4.0 * w.d * w.B * w.H * visible_pairs(w.L, w.causal, w.window)
+
+
+def algorithmic_flops_bwd(w) -> float:
+    return 2.5 * algorithmic_flops(w)
+
+
+def algorithmic_bytes_bwd(w) -> float:
+    """One read of q, k, v, out, dout (16-bit) and lse (fp32), one write of
+    dq, dk, dv (16-bit); the workspace (8 bytes per row, written and read)."""
+    return (2.0 * w.B * w.L * w.d * (4 * w.H + 4 * w.H_kv) + 4.0 * w.B * w.H * w.L
+            + 3 * 8.0 * w.B * w.H * w.L)
 
 
 def algorithmic_bytes(w) -> float:
@@ -96,6 +115,80 @@ def time_workload(w, steps: int, warmup: int):
                 peak_mem=peak, peak_mem_incl_inputs=peak, peak_mem_call=peak - base)
 
 
+def make_dout(w):
+    """The upstream gradient of the backward benchmark: seeded N(0,1), rounded."""
+    from synth import make_qkv
+    g, _, _ = make_qkv(w.B, w.H, w.H, w.L, w.d, w.dtype, 5007)
+    return g
+
+
+def time_backward(w, steps: int, warmup: int):
+    """Forward once, then time `steps` backward calls after `warmup` calls,
+    with HIP events on the stream the kernels are launched on."""
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in workload_inputs(w))
+    g = make_dout(w).to(dev)
+    stream = torch.cuda.current_stream(dev)
+    out, lse = attn.forward(q, k, v, causal=w.causal, window=w.window, scale=w.scale, stream=stream)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
+    base = torch.cuda.memory_allocated(dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(attn.attn_bwd_workspace_size(w.B, w.H, w.L), dtype=torch.uint8, device=dev)
+
+    def step():
+        attn.backward(q, k, v, out, lse, g, causal=w.causal, window=w.window, scale=w.scale,
+                      dq=dq, dk=dk, dv=dv, workspace=ws, stream=stream)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(stop) / steps
+    peak = torch.cuda.max_memory_allocated(dev)
+    return dict(ms=ms, wall_s=wall, dq=dq, inputs=(q, k, v, g), peak_mem_call=peak - base)
+
+
+def cpu_baseline_bwd(w, dq, inputs, budget_s: float = 15.0, seed: int = 7):
+    """Time the fp64 backward oracle computing dq for a seeded sample of query
+    rows for about `budget_s` seconds.  Its work is counted as 6*d FLOPs per
+    visible pair of those rows (scores, dP and dq: what it computes for them);
+    the GPU's dq on those rows is compared with it."""
+    import oracle
+    q, k, v, g = (t.cpu() for t in inputs)
+    threads = len(os.sched_getaffinity(0))
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        threads = min(threads, int(os.environ["OMP_NUM_THREADS"]))
+    rng = np.random.default_rng(seed)
+    n_total = w.B * w.H * w.L
+    order = rng.permutation(n_total)
+    done, flops, elapsed, err = 0, 0.0, 0.0, 0.0
+    flat = dq.reshape(-1, w.d)
+    batch = 32
+    while elapsed < budget_s and done < n_total:
+        rows = np.sort(order[done:done + batch])
+        t0 = time.perf_counter()
+        ref, _, _ = oracle.attention_bwd(q, k, v, g, w.dtype, w.causal, w.window, w.scale,
+                                         q_rows=rows, kv_rows=[], threads=threads)
+        elapsed += time.perf_counter() - t0
+        flops += 6.0 * w.d * float(row_visible(rows % w.L, w.L, w.causal, w.window).sum())
+        got = flat[torch.from_numpy(rows).to(flat.device)].double().cpu().numpy()
+        err = max(err, float(np.abs(got - ref).max()))
+        done += len(rows)
+        batch = min(2048, batch * 2)
+    return dict(value=flops / elapsed / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
+                sample=f"dq of {done} seeded random query rows of {n_total} ({w.name}), "
+                       f"{elapsed:.1f} s of fp64 oracle time, {flops:.3e} FLOPs (6*d per visible pair)",
+                parity_max_abs_dq=err)
+
+
 def cpu_baseline(w, out, lse, inputs, budget_s: float = 15.0, seed: int = 7):
     """Time the fp64 oracle on a seeded sample of rows for about `budget_s`
     seconds; return its throughput in the metric's unit and the GPU-vs-oracle
@@ -133,21 +226,26 @@ def cpu_baseline(w, out, lse, inputs, budget_s: float = 15.0, seed: int = 7):
 
 
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCE = os.path.join(ROOT, "exact_io_aware_25_amd", "csrc", "attn_fwd.hip")
+CSRC = os.path.join(ROOT, "exact_io_aware_25_amd", "csrc")
+KERNEL_SOURCE = os.path.join(CSRC, "attn_fwd.hip")
+KERNEL_SOURCE_BWD = os.path.join(CSRC, "attn_bwd.hip")
 
 
-def kernel_source_sha256() -> str:
+def kernel_source_sha256(path: str = KERNEL_SOURCE) -> str:
+    """Hash of a kernel source followed by the shared header it includes."""
     import hashlib
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    h = hashlib.sha256(open(path, "rb").read())
+    h.update(open(os.path.join(CSRC, "attn_common.h"), "rb").read())
+    return h.hexdigest()
 
 
-def profiled_traffic(w):
+def profiled_traffic(w, kind: str = "attn_fwd", source: str = KERNEL_SOURCE):
     """Bytes per launch between L2 and memory for this workload, from the
     committed rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE per
     dispatch, each scaled by what the counter reads for a plain device copy
     of known size); None when there is no summary for this workload or the
     kernel source has changed since it was taken."""
-    path = os.path.join(PROFILES, f"attn_fwd_{w.name}_traffic.txt")
+    path = os.path.join(PROFILES, f"{kind}_{w.name}_traffic.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -155,7 +253,7 @@ def profiled_traffic(w):
         if "=" in line and not line.lstrip().startswith("#"):
             key, val = line.split("=", 1)
             vals[key.strip()] = val.strip()
-    if vals.get("workload") != w.name or vals.get("kernel_source_sha256") != kernel_source_sha256():
+    if vals.get("workload") != w.name or vals.get("kernel_source_sha256") != kernel_source_sha256(source):
         return None
     copy_bytes = float(vals["copy_bytes"])
     fetch_scale = copy_bytes / (float(vals["copy_fetch_kib"]) * 1024)
@@ -187,6 +285,8 @@ def main():
                     help="also time every workload and print one extra JSON line each (to stderr)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (attn_bwd) on the workload instead of the forward")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, run one plain device copy of this many MiB (a reference "
                          "kernel of known traffic for scaling profiler byte counters)")
@@ -208,6 +308,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.backward:
+        main_backward(w, args)
+        return
     r = time_workload(w, args.steps, args.warmup)
     flops = algorithmic_flops(w)
     tflops = flops / (r["ms"] * 1e-3) / 1e12
@@ -260,6 +363,38 @@ def main():
                                            "slope_time": round(loglog_slope(Ls, ts), 3),
                                            "slope_memory": round(loglog_slope(Ls, ms_), 3)}}),
               file=sys.stderr, flush=True)
+
+
+def main_backward(w, args):
+    r = time_backward(w, args.steps, args.warmup)
+    flops = algorithmic_flops_bwd(w)
+    tflops = flops / (r["ms"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC_BWD if w.name == DEFAULT_WORKLOAD else f"attn bwd TFLOP/s ({w.name})",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: seeded iid N(0,1) q, k, v and upstream gradient, rounded to the 16-bit type",
+        "config": {"workload": w.name, "pass": "backward", "B": w.B, "H": w.H, "H_kv": w.H_kv, "L": w.L,
+                   "d": w.d, "causal": w.causal, "window": w.window, "scale": w.scale,
+                   "algorithmic_flops": flops, "pct_of_mfma_peak": round(100 * tflops / MFMA_PEAK_F16_TFLOPS, 2),
+                   "peak_mem_call_bytes": r["peak_mem_call"], "algorithmic_bytes": algorithmic_bytes_bwd(w),
+                   "launches_per_step": 3},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_F16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_F16_TFLOPS, 4),
+                     "traffic": profiled_traffic(w, "attn_bwd", KERNEL_SOURCE_BWD),
+                     "scope": "one attn_bwd call (prep, dK/dV and dQ kernels)"},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_bwd(w, r["dq"], r["inputs"], args.cpu_budget)
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

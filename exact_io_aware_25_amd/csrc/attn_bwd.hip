@@ -14,7 +14,7 @@
 //   dv_j  = sum_i P_ij dO_i,  dk_j = scale sum_i dS_ij q_i,  dq_i = scale sum_j dS_ij k_j
 //
 // Three kernels on the caller's stream:
-//   1. prep: per query row, -lse*log2(e) and D into the workspace;
+//   1. prep: per query row, -lse*log2(e) and -D into the workspace;
 //   2. dK/dV: a workgroup owns 32*NW keys of one K/V head and walks the
 //      query tiles of every query head that reads it.  K and V fragments stay
 //      in registers (B operands); Q and dO tiles stream through LDS.  Per
@@ -47,7 +47,7 @@ constexpr int kTileQ = 64;  // query rows per LDS tile of the dK/dV kernel
 struct BwdParams {
     const void *q, *k, *v, *o, *dout;
     const float *lse;
-    float *ws;          // per (b, h): Lp floats of -lse*log2(e), then Lp floats of D
+    float *ws;          // per (b, h): Lp floats of -lse*log2(e), then Lp floats of -D
     void *dq, *dk, *dv;
     int B, H, H_kv, L;
     int Lp;             // L rounded up to a multiple of kTileQ
@@ -59,9 +59,10 @@ struct BwdParams {
 };
 
 // ---------------------------------------------------------------- 1. prep
-// One row of D/8 16-byte pieces per D/8 consecutive lanes.  Rows L..Lp-1 of
-// each (b, h) get zeros, so every workspace value the dK/dV kernel can read
-// is finite.
+// One row of D/8 16-byte pieces per D/8 consecutive lanes.  The workspace
+// gets -lse*log2(e) and -D (negated so that both enter the kernels as
+// addends).  Rows L..Lp-1 of each (b, h) get zeros, so every workspace value
+// the dK/dV kernel can read is finite.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdParams p)
 {
@@ -86,20 +87,23 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(BwdParams p)
     if (piece == 0 && bh < (int64_t)p.B * p.H) {
         float *w = p.ws + bh * 2 * p.Lp;
         w[i] = live ? -p.lse[bh * p.L + i] * kLog2e : 0.f;
-        w[p.Lp + i] = acc;
+        w[p.Lp + i] = -acc;
     }
 }
 
 // ---------------------------------------------------------------- 2. dK, dV
+// At d=64 the register budget is held to three waves per SIMD (one more
+// than the unconstrained allocation): measured faster, the extra wave hides
+// LDS latency.  At d=128 the accumulators alone need the whole file.
 template <typename T, int D, bool CAUSAL, bool WINDOW, int NW>
-__global__ __launch_bounds__(64 * NW) void attn_bwd_dkdv_kernel(BwdParams p)
+__global__ __launch_bounds__(64 * NW, D == 64 ? 12 / NW : 1) void attn_bwd_dkdv_kernel(BwdParams p)
 {
     typedef typename Vec8<T>::type vec8;
     constexpr int kThreads = 64 * NW;
     constexpr int kBlockKV = kRowsPerWave * NW;          // keys per workgroup
     constexpr int kRowBytes = 2 * D;
     constexpr int kTileBytes = kTileQ * kRowBytes;       // one Q or dO tile
-    constexpr int kWsBytes = 1024;                       // -lse*log2e and D of 64 rows, + zero fill
+    constexpr int kWsBytes = 1024;                       // -lse*log2e and -D of 64 rows, + zero fill
     constexpr int kStageBytes = 2 * kTileBytes + kWsBytes;
     constexpr int kUnits = D / 8;
     constexpr int kChunks = kTileQ * kUnits / kThreads;  // 16-byte units per thread per tile
@@ -244,7 +248,10 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dkdv_kernel(BwdParams p)
         for (int qb = 0; qb < 2; ++qb) {
             // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys;
             // register r of lane half hi holds query q0 + 32qb + 16(r/8) + 8hi + r%8
-            f32x16 s = f32x16{}, dp = f32x16{};
+            // dP starts from -D (read straight from LDS), so the products give dP - D
+            f32x16 s = f32x16{}, dp;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dp[r] = tw[kTileQ + 32 * qb + 16 * (r / 8) + 8 * hi + (r % 8)];
             {
                 vec8 af[kDSteps], gf[kDSteps];
 #pragma unroll
@@ -273,9 +280,8 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dkdv_kernel(BwdParams p)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float lse2n = tw[base + e];
-                    const float dval = tw[kTileQ + base + e];
                     pf[e] = __builtin_amdgcn_exp2f(fmaf(s[8 * t + e], p.scale_log2, lse2n));
-                    df[e] = pf[e] * (dp[8 * t + e] - dval);
+                    df[e] = pf[e] * dp[8 * t + e];
                 }
                 pv[t] = __builtin_convertvector(pf, vec8);
                 dsv[t] = __builtin_convertvector(df, vec8);
@@ -392,7 +398,7 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_kernel(BwdParams p)
         }
     }
     const float lse2n = qi < L ? wsh[qi] : 0.f;
-    const float dval = qi < L ? wsh[p.Lp + qi] : 0.f;
+    const float negd = qi < L ? wsh[p.Lp + qi] : 0.f;  // -D of this lane's row
     f32x16 acc_dq[kDBlocks];
 #pragma unroll
     for (int i = 0; i < kDBlocks; ++i) acc_dq[i] = f32x16{};
@@ -500,7 +506,7 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_kernel(BwdParams p)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float pe = __builtin_amdgcn_exp2f(fmaf(s[ks / 2][8 * (ks % 2) + e], p.scale_log2, lse2n));
-                df[e] = pe * (dp[ks / 2][8 * (ks % 2) + e] - dval);
+                df[e] = pe * (dp[ks / 2][8 * (ks % 2) + e] + negd);
             }
             dsv[ks] = __builtin_convertvector(df, vec8);
         }

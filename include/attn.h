@@ -126,8 +126,8 @@ int attn_launch_shape(int B, int H, int L, int d, int causal, int window, int *w
  * 16-bit type, each element rounded once from an fp32 accumulator.
  * workspace: caller-owned device memory of attn_bwd_workspace_size(B, H, L)
  * bytes, 16-byte aligned; on return it holds, per (b, h), Lp values of
- * -lse*log2(e) followed by Lp values of D (Lp = L rounded up to a multiple of
- * 64; the padding rows hold zeros), in fp32.
+ * -lse*log2(e) followed by Lp values of -D (Lp = L rounded up to a multiple
+ * of 64; the padding rows hold zeros), in fp32.
  * Behaviour as for attn_fwd: device pointers, enqueue on `stream` and return,
  * no allocation, no synchronisation, arguments checked before any HIP call,
  * B = 0 or L = 0 is an empty problem.  dq, dk, dv and workspace must not

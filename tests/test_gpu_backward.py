@@ -262,8 +262,8 @@ def test_bwd_batch_independence():
 
 
 def test_bwd_workspace_contents():
-    """The workspace holds -lse*log2(e) (fp32, bitwise) and D = dout.out per
-    row (fp32 sum of 16-bit products), with zeros in the padding rows."""
+    """The workspace holds -lse*log2(e) (fp32, bitwise) and -D = -dout.out
+    per row (fp32 sum of 16-bit products), with zeros in the padding rows."""
     B, H, H_kv, L, d = 2, 3, 3, 100, 64
     announce("bwd workspace")
     q, k, v = make_qkv(B, H, H_kv, L, d, "f16", 23)
@@ -275,7 +275,7 @@ def test_bwd_workspace_contents():
     want = -(lse * torch.tensor(LOG2E, dtype=torch.float32))
     assert torch.equal(ws[:, 0, :L], want)
     dsum = (res["out"].double() * g.double()).sum(-1).reshape(B * H, L)
-    assert torch.allclose(ws[:, 1, :L].double(), dsum, rtol=1e-5, atol=1e-5)
+    assert torch.allclose(-ws[:, 1, :L].double(), dsum, rtol=1e-5, atol=1e-5)
     assert torch.all(ws[:, :, L:] == 0)
 
 

@@ -67,3 +67,42 @@ def test_planted_mistake_is_caught(name, tmp_path):
             if len(caught) >= 1:
                 break
     assert caught, f"no pin caught the planted mistake {name}"
+
+
+PAGED_MUTANTS = {
+    "paged_top_left_alignment": ("p = n - Lq + i", "p = i"),
+    "paged_page_index": ("cache[block_table[b, j // block_size], g, j % block_size]",
+                         "cache[block_table[b, j % block_size], g, j // block_size]"),
+    "paged_window_off_by_one": ("lo = 0 if window < 0 else max(0, p - window)",
+                                "lo = 0 if window < 0 else max(0, p - window + 1)"),
+    "paged_scale_dropped": ("s = sc * (keys[lo:p + 1] @ qd[b, h, i])", "s = keys[lo:p + 1] @ qd[b, h, i]"),
+    "paged_last_key_dropped": ("s = sc * (keys[lo:p + 1] @ qd[b, h, i])", "s = sc * (keys[lo:p] @ qd[b, h, i])"),
+    "paged_no_normalisation": ("out[b, h, i] = (w @ vals[lo:p + 1]) / w.sum()", "out[b, h, i] = w @ vals[lo:p + 1]"),
+    "paged_lse_without_max": ("lse[b, h, i] = m + np.log(w.sum())", "lse[b, h, i] = np.log(w.sum())"),
+    "paged_gqa_interleaved": ("for h in range(g * group, (g + 1) * group):", "for h in range(g, H, H_kv):"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PAGED_MUTANTS))
+def test_planted_paged_mistake_is_caught(name, tmp_path):
+    import importlib.util
+
+    import oracle_paged_pins
+    from oracle import paged
+    old, new = PAGED_MUTANTS[name]
+    src = open(paged.__file__).read()
+    assert src.count(old) == 1, f"mutation anchor not found once: {old!r}"
+    path = os.path.join(tmp_path, "paged_mutant.py")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    spec = importlib.util.spec_from_file_location("paged_mutant", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    caught = []
+    for pin in oracle_paged_pins.ALL_PAGED_PINS:
+        try:
+            pin(mod)
+        except (AssertionError, ValueError, IndexError):
+            caught.append(pin.__name__)
+            break
+    assert caught, f"no pin caught the planted mistake {name}"

@@ -2,6 +2,7 @@
 import pytest
 
 import oracle_bwd_pins
+import oracle_paged_pins
 import oracle_pins
 
 
@@ -42,3 +43,9 @@ def test_oracle_rejects_bad_arguments(oracle_lib):
     k = np.zeros((1, 2, 4, 64), np.uint16)
     with pytest.raises(ValueError):
         oracle.attention(q, k, k, "f16", True, -1, 0.125, lib=oracle_lib)   # 3 % 2 != 0
+
+
+@pytest.mark.parametrize("pin", oracle_paged_pins.ALL_PAGED_PINS, ids=lambda f: f.__name__)
+def test_paged_pin(pin):
+    from oracle import paged
+    pin(paged)

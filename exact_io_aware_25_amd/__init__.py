@@ -1,4 +1,4 @@
-"""Exact IO-aware attention (forward and backward) for AMD MI355X (gfx950).
+"""Exact IO-aware attention (forward, backward, paged decode) for AMD MI355X (gfx950).
 
 A thin ctypes binding over the C ABI declared in ``include/attn.h``.  The
 names match the C entry points; this module only marshals arguments.  Every
@@ -30,6 +30,7 @@ ATTN_ERR_SCALE = 9
 ATTN_ERR_ALIGN = 10
 
 EXPORTS = ("attn_fwd", "attn_fwd_bf16", "attn_bwd", "attn_bwd_bf16", "attn_bwd_workspace_size",
+           "attn_decode", "attn_decode_bf16", "attn_decode_workspace_size",
            "attn_launch_shape", "attn_status_string", "attn_resolve_scale")
 
 _lib = None
@@ -63,6 +64,13 @@ def library():
             fn = getattr(lib, name)
             fn.restype = ctypes.c_int
             fn.argtypes = bsig
+        dsig = [ctypes.c_void_p] * 8 + [ctypes.c_int] * 10 + [ctypes.c_float, ctypes.c_void_p]
+        for name in ("attn_decode", "attn_decode_bf16"):
+            fn = getattr(lib, name)
+            fn.restype = ctypes.c_int
+            fn.argtypes = dsig
+        lib.attn_decode_workspace_size.restype = ctypes.c_size_t
+        lib.attn_decode_workspace_size.argtypes = [ctypes.c_int] * 6
         lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
         lib.attn_bwd_workspace_size.argtypes = [ctypes.c_int] * 3
         lib.attn_status_string.restype = ctypes.c_char_p
@@ -101,6 +109,25 @@ def attn_bwd_bf16(q, k, v, out, dout, lse, dq, dk, dv, workspace, B, H, H_kv, L,
 
 def attn_bwd_workspace_size(B, H, L) -> int:
     return int(library().attn_bwd_workspace_size(int(B), int(H), int(L)))
+
+
+def attn_decode(q, k_cache, v_cache, block_table, seq_lens, out, lse, workspace, B, H, H_kv, Lq, d, block_size,
+                max_blocks_per_seq, num_blocks, max_seq_len, window, scale, stream) -> int:
+    """fp16 decode entry point; pointers are integer device addresses."""
+    return library().attn_decode(q, k_cache, v_cache, block_table, seq_lens, out, lse, workspace, B, H, H_kv, Lq,
+                                 d, block_size, max_blocks_per_seq, num_blocks, max_seq_len, window, scale, stream)
+
+
+def attn_decode_bf16(q, k_cache, v_cache, block_table, seq_lens, out, lse, workspace, B, H, H_kv, Lq, d,
+                     block_size, max_blocks_per_seq, num_blocks, max_seq_len, window, scale, stream) -> int:
+    """bf16 decode entry point; same arguments as ``attn_decode``."""
+    return library().attn_decode_bf16(q, k_cache, v_cache, block_table, seq_lens, out, lse, workspace, B, H, H_kv,
+                                      Lq, d, block_size, max_blocks_per_seq, num_blocks, max_seq_len, window, scale,
+                                      stream)
+
+
+def attn_decode_workspace_size(B, H, H_kv, Lq, d, max_seq_len) -> int:
+    return int(library().attn_decode_workspace_size(int(B), int(H), int(H_kv), int(Lq), int(d), int(max_seq_len)))
 
 
 def attn_status_string(status: int) -> str:
@@ -219,3 +246,54 @@ def backward(q, k, v, out, lse, dout, causal: bool = False, window: int = -1, sc
                     int(bool(causal)), int(window), 0.0 if scale is None else float(scale), stream.cuda_stream)
     _check(status)
     return dq, dk, dv
+
+
+def decode(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int, window: int = -1, scale=None,
+           out=None, lse=None, workspace=None, stream=None):
+    """Attention of the Lq newest tokens of each sequence over a paged KV cache.
+
+    q [B,H,Lq,d]; k_cache, v_cache [num_blocks,H_kv,block_size,d] (fp16 or
+    bf16, on the GPU); block_table int32 [B, max_blocks]; seq_lens int32 [B]
+    on the GPU; ``max_seq_len`` bounds seq_lens (host int).  Returns (out
+    [B,H,Lq,d], lse [B,H,Lq] fp32).  Launches on ``stream`` (default: torch's
+    current stream).
+    """
+    import torch
+
+    if q.dim() != 4 or k_cache.dim() != 4 or v_cache.dim() != 4:
+        raise ValueError("q must be [B,H,Lq,d] and the caches [num_blocks,H_kv,block_size,d]")
+    if q.dtype not in (torch.float16, torch.bfloat16) or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise ValueError("q and the caches must share one dtype, float16 or bfloat16")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32 or block_table.dim() != 2:
+        raise ValueError("block_table must be int32 [B, max_blocks] and seq_lens int32 [B]")
+    tensors = (q, k_cache, v_cache, block_table, seq_lens)
+    if not q.is_cuda or any(t.device != q.device for t in tensors):
+        raise ValueError("all tensors must be on the same GPU device")
+    if not all(t.is_contiguous() for t in tensors):
+        raise ValueError("all tensors must be contiguous")
+    B, H, Lq, d = q.shape
+    num_blocks, H_kv, block_size, _ = k_cache.shape
+    if (tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.shape[3] != d or block_table.shape[0] != B
+            or tuple(seq_lens.shape) != (B,)):
+        raise ValueError("shape mismatch between q, caches, block_table and seq_lens")
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device) if lse is None else lse
+    if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if tuple(lse.shape) != (B, H, Lq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, Lq]")
+    need = attn_decode_workspace_size(B, H, H_kv, Lq, d, max_seq_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must hold {need} bytes")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    fn = attn_decode if q.dtype == torch.float16 else attn_decode_bf16
+    with torch.cuda.device(q.device):
+        status = fn(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+                    seq_lens.data_ptr(), out.data_ptr(), lse.data_ptr(), workspace.data_ptr(), B, H, H_kv, Lq, d,
+                    block_size, block_table.shape[1], num_blocks, int(max_seq_len), int(window),
+                    0.0 if scale is None else float(scale), stream.cuda_stream)
+    _check(status)
+    return out, lse

@@ -1,6 +1,6 @@
 /*
- * attn.h -- C ABI of exact attention (forward and backward passes) for AMD
- * MI355X (gfx950).
+ * attn.h -- C ABI of exact attention (forward, backward and paged decode) for
+ * AMD MI355X (gfx950).
  *
  * The operation is exact scaled-dot-product attention computed the
  * IO-aware way: Q, K and V are streamed through on-chip tiles, the softmax is
@@ -148,6 +148,50 @@ int attn_bwd_bf16(const void *q, const void *k, const void *v, const void *out, 
 /* Bytes of workspace attn_bwd / attn_bwd_bf16 need for B, H, L
  * (8 * B * H * Lp); 0 if any of them is <= 0.  Host-only. */
 size_t attn_bwd_workspace_size(int B, int H, int L);
+
+/*
+ * Decode: attention of the Lq newest tokens of each sequence over its KV
+ * cache, kept in fixed-size blocks behind a page table.  Each generated token
+ * reads its whole cache, which makes this step HBM-bound («Что такое
+ * memory-efficient attention для long context на 8x H100?», section 1); the
+ * paged layout is PagedAttention's (same page, section 3: blocks of e.g. 16
+ * tokens, a page table from logical to physical blocks).  With n = seq_lens[b]
+ * and p = n - Lq + i the position of new token i (the last query aligned with
+ * the last key), query (b, h, i) sees keys j <= p with, if window >= 0,
+ * p - j <= window, of K/V head g = h / (H / H_kv); out and lse are the forward
+ * definition over those keys (rows with p < 0 see no key: out 0, lse -inf).
+ *
+ * Layout:
+ *   q, out          : [B, H, Lq, d]   16-bit (fp16 for attn_decode, bf16 for attn_decode_bf16)
+ *   k_cache, v_cache: [num_blocks, H_kv, block_size, d]; key j of sequence b is row
+ *                     j % block_size of block block_table[b][j / block_size]
+ *   block_table     : int32 [B, max_blocks_per_seq]
+ *   seq_lens        : int32 [B], device memory; values are clamped to [0, max_seq_len]
+ *   lse             : [B, H, Lq] fp32, natural log
+ *   workspace       : attn_decode_workspace_size(B, H, H_kv, Lq, d, max_seq_len) bytes
+ *                     (per-chunk partial results; contents undefined on return)
+ * block_size: a power of two in [16, 4096]; max_seq_len <= max_blocks_per_seq *
+ * block_size.  Table entries are clamped to [0, num_blocks - 1], so an
+ * invalid table reads wrong blocks but never outside the cache.
+ * Behaviour as for attn_fwd (device pointers, enqueue only, no allocation, no
+ * synchronisation, arguments checked before any HIP call; B = 0 is empty).
+ * out, lse and workspace must not overlap one another or any input; q, the
+ * caches, out and workspace 16-byte aligned, the int32 arrays and lse 4-byte.
+ */
+int attn_decode(const void *q, const void *k_cache, const void *v_cache, const int *block_table,
+                const int *seq_lens, void *out, float *lse, void *workspace,
+                int B, int H, int H_kv, int Lq, int d, int block_size, int max_blocks_per_seq,
+                int num_blocks, int max_seq_len, int window, float scale, void *stream);
+
+/* The same decode step for bfloat16 q, caches and out. */
+int attn_decode_bf16(const void *q, const void *k_cache, const void *v_cache, const int *block_table,
+                     const int *seq_lens, void *out, float *lse, void *workspace,
+                     int B, int H, int H_kv, int Lq, int d, int block_size, int max_blocks_per_seq,
+                     int num_blocks, int max_seq_len, int window, float scale, void *stream);
+
+/* Bytes of workspace attn_decode / attn_decode_bf16 need; 0 for invalid
+ * arguments.  Host-only. */
+size_t attn_decode_workspace_size(int B, int H, int H_kv, int Lq, int d, int max_seq_len);
 
 /* The fp32 scale the kernels use for a given scale argument and head size:
  * `scale` itself when finite and > 0, else the fp32 value nearest 1/sqrt(d).

@@ -110,3 +110,91 @@ def sample_rows(B: int, H: int, L: int, n_random: int, seed: int, tile: int = 64
         for i in sorted(set(base) | set(rnd)):
             out.append(bh * L + i)
     return out
+
+
+# ---------------------------------------------------------------- decode over a paged KV cache
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """Lq new queries per sequence against a paged KV cache.
+
+    Sequence lengths are drawn uniformly from [len_min, len_max] (seeded), so
+    a batch is ragged as a serving batch is; each sequence's cache is cut into
+    `block_size`-token blocks placed at seeded random physical blocks of one
+    pool, as PagedAttention places them («Что такое memory-efficient attention
+    для long context на 8x H100?», section 3: fixed-size blocks, e.g. 16
+    tokens, behind a page table)."""
+    name: str
+    B: int
+    H: int
+    H_kv: int
+    d: int
+    dtype: str
+    Lq: int
+    len_min: int
+    len_max: int
+    block_size: int
+    window: int
+    scale: float
+    seed: int
+
+
+#   decode_128k_gqa: the long-context case of «Что такое memory-efficient attention
+#                    для long context на 8x H100?» (section 1: every generated token
+#                    reads the whole KV cache): 8 sequences of 64k-128k tokens, 32
+#                    query heads over 8 K/V heads, head_dim 128, bf16, 16-token blocks.
+#   decode_128k_h4:  one decode step of the headline shape (causal, 4 heads, head_dim
+#                    64, fp16) at 131072 tokens.
+#   decode_32k_spec: 32 sequences of 8k-32k tokens, 4 new queries each (several tokens
+#                    per step), GQA 32/8, head_dim 128, bf16, 32-token blocks.
+#   decode_64k_swa:  sliding-window decode (window 4096, «Оптимизация внимания
+#                    Flash», Workflow 2, Step 3) over 4 sequences of 32k-64k tokens.
+DECODE_WORKLOADS = {
+    w.name: w for w in [
+        DecodeWorkload("decode_128k_gqa", 8, 32, 8, 128, "bf16", 1, 65536, 131072, 16, -1, _INV_SQRT_128, 2000),
+        DecodeWorkload("decode_128k_h4", 1, 4, 4, 64, "f16", 1, 131072, 131072, 16, -1, 0.125, 2001),
+        DecodeWorkload("decode_32k_spec", 32, 32, 8, 128, "bf16", 4, 8192, 32768, 32, -1, _INV_SQRT_128, 2002),
+        DecodeWorkload("decode_64k_swa", 4, 32, 8, 128, "bf16", 1, 32768, 65536, 16, 4096, _INV_SQRT_128, 2003),
+    ]
+}
+
+
+def make_paged(B: int, H: int, H_kv: int, d: int, dtype: str, Lq: int, lens, block_size: int, seed: int,
+               spare_blocks: int = 3):
+    """Inputs of a decode step: q [B,H,Lq,d]; k_cache, v_cache
+    [num_blocks, H_kv, block_size, d] of iid N(0,1) rounded to `dtype` (blocks
+    no sequence uses hold draws too); block_table int32 [B, max_blocks] with
+    each sequence's blocks at seeded random distinct physical blocks (unused
+    entries -1); seq_lens int32 [B]."""
+    gen = torch.Generator(device="cpu").manual_seed(int(seed))
+    tdt = TORCH_DTYPES[dtype]
+    lens = [int(n) for n in lens]
+    per_seq = [(n + block_size - 1) // block_size for n in lens]
+    num_blocks = sum(per_seq) + spare_blocks
+    q = torch.randn((B, H, Lq, d), generator=gen, dtype=torch.float32).to(tdt)
+    k_cache = torch.empty((num_blocks, H_kv, block_size, d), dtype=tdt)
+    v_cache = torch.empty((num_blocks, H_kv, block_size, d), dtype=tdt)
+    step = max(1, (1 << 24) // (H_kv * block_size * d))  # draw in bounded chunks
+    for cache in (k_cache, v_cache):
+        for s in range(0, num_blocks, step):
+            e = min(num_blocks, s + step)
+            cache[s:e] = torch.randn((e - s, H_kv, block_size, d), generator=gen, dtype=torch.float32).to(tdt)
+    perm = torch.randperm(num_blocks, generator=gen)
+    width = max(per_seq)
+    table = torch.full((B, width), -1, dtype=torch.int32)
+    used = 0
+    for b, nb in enumerate(per_seq):
+        table[b, :nb] = perm[used:used + nb].to(torch.int32)
+        used += nb
+    return q, k_cache, v_cache, table, torch.tensor(lens, dtype=torch.int32)
+
+
+def decode_lens(w: DecodeWorkload):
+    """The workload's seeded sequence lengths (each >= Lq)."""
+    gen = torch.Generator(device="cpu").manual_seed(int(w.seed) + 1)
+    if w.len_min == w.len_max:
+        return [w.len_max] * w.B
+    return torch.randint(w.len_min, w.len_max + 1, (w.B,), generator=gen).tolist()
+
+
+def decode_inputs(w: DecodeWorkload):
+    return make_paged(w.B, w.H, w.H_kv, w.d, w.dtype, w.Lq, decode_lens(w), w.block_size, w.seed)

@@ -90,7 +90,7 @@ def test_binding_does_not_import_the_oracle():
     import sys
     src = open(os.path.join(ROOT, "exact_io_aware_25_amd", "__init__.py")).read()
     assert "oracle" not in src.replace("no fallback", "")
-    for name in ("attn_fwd.hip", "attn_bwd.hip", "attn_common.h"):
+    for name in ("attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_common.h"):
         hip = open(os.path.join(ROOT, "exact_io_aware_25_amd", "csrc", name)).read()
         assert "oracle" not in hip, name
 
@@ -172,3 +172,48 @@ def test_backward_workspace_size():
     assert attn.attn_bwd_workspace_size(0, 4, 256) == 0
     assert attn.attn_bwd_workspace_size(1, 4, 0) == 0
     assert attn.attn_bwd_workspace_size(1, -1, 5) == 0
+
+
+# fake addresses for the decode tensors
+DQ_, KC, VC, BT, SL, DO_, DL, DW = (0x30000000 + i * (1 << 24) for i in range(8))
+
+
+def call_dec(fn=attn.attn_decode, q=DQ_, kc=KC, vc=VC, bt=BT, sl=SL, o=DO_, lse=DL, ws=DW, B=2, H=8, H_kv=2,
+             Lq=1, d=128, bs=16, max_blocks=64, num_blocks=128, max_len=1024, window=-1, scale=0.0):
+    return fn(q, kc, vc, bt, sl, o, lse, ws, B, H, H_kv, Lq, d, bs, max_blocks, num_blocks, max_len, window,
+              scale, None)
+
+
+@pytest.mark.parametrize("fn", [attn.attn_decode, attn.attn_decode_bf16])
+def test_decode_argument_errors(fn):
+    for name in ("q", "kc", "vc", "bt", "sl", "o", "lse", "ws"):
+        assert call_dec(fn, **{name: 0}) == attn.ATTN_ERR_NULL, name
+    assert call_dec(fn, H=7) == attn.ATTN_ERR_SHAPE
+    assert call_dec(fn, Lq=0) == attn.ATTN_ERR_SHAPE
+    assert call_dec(fn, bs=24) == attn.ATTN_ERR_SHAPE            # not a power of two
+    assert call_dec(fn, bs=8) == attn.ATTN_ERR_SHAPE
+    assert call_dec(fn, max_len=64 * 16 + 1) == attn.ATTN_ERR_SHAPE   # beyond the table's reach
+    assert call_dec(fn, max_len=0) == attn.ATTN_ERR_SHAPE
+    assert call_dec(fn, num_blocks=0) == attn.ATTN_ERR_SHAPE
+    assert call_dec(fn, d=96) == attn.ATTN_ERR_HEAD_DIM
+    assert call_dec(fn, window=-2) == attn.ATTN_ERR_WINDOW
+    assert call_dec(fn, scale=float("inf")) == attn.ATTN_ERR_SCALE
+    assert call_dec(fn, o=DQ_) == attn.ATTN_ERR_ALIAS
+    assert call_dec(fn, ws=KC + 4096) == attn.ATTN_ERR_ALIAS
+    assert call_dec(fn, lse=SL) == attn.ATTN_ERR_ALIAS
+    assert call_dec(fn, ws=DO_) == attn.ATTN_ERR_ALIAS
+    assert call_dec(fn, q=DQ_ + 8) == attn.ATTN_ERR_ALIGN
+    assert call_dec(fn, bt=BT + 2) == attn.ATTN_ERR_ALIGN
+    assert call_dec(fn, ws=DW + 4) == attn.ATTN_ERR_ALIGN
+    assert call_dec(fn, q=0, kc=0, vc=0, bt=0, sl=0, o=0, lse=0, ws=0, B=0) == attn.ATTN_OK
+    assert call_dec(fn, num_blocks=(1 << 31) - 1, H_kv=1 << 20, H=1 << 20, bs=4096, max_blocks=1 << 20,
+                    max_len=1 << 30) == attn.ATTN_ERR_SIZE    # cache bytes beyond 2^62
+
+
+def test_decode_workspace_size():
+    ws = attn.attn_decode_workspace_size
+    assert ws(1, 4, 4, 1, 64, 131072) > 0
+    assert ws(8, 32, 8, 1, 128, 131072) % 16 == 0
+    assert ws(0, 4, 4, 1, 64, 100) == 0 and ws(1, 3, 2, 1, 64, 100) == 0 and ws(1, 4, 4, 1, 96, 100) == 0
+    # partial results of every chunk: at least one (O, m, l) per query row
+    assert ws(2, 8, 2, 3, 64, 100) >= 2 * 8 * 3 * (64 + 2) * 4

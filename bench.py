@@ -12,6 +12,11 @@ GPU outputs are also checked against it).
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--sweep]
     python bench.py --backward [...]
 
+With --decode, one step is one attn_decode call (the newest Lq tokens of
+each sequence of a decode workload over its paged KV cache); the metric is
+bytes: the K/V rows every query row must see, read once per K/V head, plus q,
+out and lse, per second, against the HBM peak.
+
 With --backward, one step is one attn_bwd call (dq, dk, dv for an upstream
 gradient, from the forward's out and lse) on the same workload, and the line
 reports the backward's throughput: algorithmic FLOPs 10*d per visible pair
@@ -33,12 +38,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import exact_io_aware_25_amd as attn  # noqa: E402
-from synth import WORKLOADS, workload_inputs  # noqa: E402
+from synth import DECODE_WORKLOADS, WORKLOADS, decode_inputs, decode_lens, workload_inputs  # noqa: E402
 
 MFMA_PEAK_F16_TFLOPS = 2516.6   # MI355X dense fp16/bf16: 256 CU x 4096 FLOP/clk x 2.4 GHz
 HBM_PEAK_GBS = 8000.0
 METRIC = "causal attn fwd TFLOP/s @ L=128k,H=4,d=64 fp16; % of MFMA peak"
 METRIC_BWD = "causal attn bwd TFLOP/s @ L=128k,H=4,d=64 fp16; % of MFMA peak"
+METRIC_DECODE = "paged decode GB/s @ 8 x 64k-128k tokens, H=32/8, d=128 bf16; % of HBM peak"
+DEFAULT_DECODE = "decode_128k_gqa"
 DEFAULT_WORKLOAD = "causal_128k_h4"
 
 
@@ -113,6 +120,76 @@ def time_workload(w, steps: int, warmup: int):
     peak = torch.cuda.max_memory_allocated(dev)
     return dict(ms=ms, wall_s=wall, out=out, lse=lse, inputs=(q, k, v),
                 peak_mem=peak, peak_mem_incl_inputs=peak, peak_mem_call=peak - base)
+
+
+def decode_bytes(w) -> float:
+    """Algorithmic bytes of one decode step: every K/V row some query row
+    sees, once per K/V head, plus q and out (16-bit), lse (fp32), the page
+    table entries and lengths."""
+    kv = 0
+    for n in decode_lens(w):
+        first = max(0, n - w.Lq - w.window) if w.window >= 0 else 0
+        kv += (n - first) * w.H_kv * w.d * 2 * 2
+        kv += 4 * ((n + w.block_size - 1) // w.block_size) + 4
+    rows = w.B * w.H * w.Lq
+    return float(kv + rows * w.d * 2 * 2 + rows * 4)
+
+
+def time_decode(w, steps: int, warmup: int):
+    dev = torch.device("cuda:0")
+    q, kc, vc, bt, sl = (t.to(dev) for t in decode_inputs(w))
+    max_len = max(decode_lens(w))
+    stream = torch.cuda.current_stream(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    ws = torch.empty(attn.attn_decode_workspace_size(w.B, w.H, w.H_kv, w.Lq, w.d, max_len), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        attn.decode(q, kc, vc, bt, sl, max_len, window=w.window, scale=w.scale, out=out, lse=lse,
+                    workspace=ws, stream=stream)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return dict(ms=start.elapsed_time(stop) / steps, out=out, lse=lse, workspace_bytes=ws.numel(),
+                inputs=(q, kc, vc, bt, sl))
+
+
+def cpu_baseline_decode(w, out, inputs, budget_s: float = 15.0):
+    """The fp64 paged oracle (NumPy, BLAS threads up to the host cores) on
+    whole sequences, in order, for about `budget_s` seconds; its throughput in
+    the metric's bytes, and the GPU's error on those sequences."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import paged
+    q, kc, vc, bt, sl = (t.cpu() for t in inputs)
+    lens = decode_lens(w)
+    threads = len(os.sched_getaffinity(0))
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        threads = min(threads, int(os.environ["OMP_NUM_THREADS"]))
+    done, nbytes, elapsed, err = 0, 0.0, 0.0, 0.0
+    with threadpool_limits(limits=threads):
+        while done < w.B and elapsed < budget_s:
+            b = done
+            t0 = time.perf_counter()
+            ro, _ = paged.decode_attention(q[b:b + 1], kc, vc, bt[b:b + 1].numpy(), [lens[b]], w.dtype,
+                                           w.window, w.scale)
+            elapsed += time.perf_counter() - t0
+            n = lens[b]
+            first = max(0, n - w.Lq - w.window) if w.window >= 0 else 0
+            nbytes += (n - first) * w.H_kv * w.d * 4 + w.H * w.Lq * (w.d * 4 + 4)
+            err = max(err, float(np.abs(out[b:b + 1].double().cpu().numpy() - ro).max()))
+            done += 1
+    return dict(value=nbytes / elapsed / 1e9, unit="GB/s", cores=threads, kind="oracle",
+                sample=f"{done} of {w.B} sequences of {w.name}, {elapsed:.1f} s of fp64 oracle time",
+                parity_max_abs_o=err)
 
 
 def make_dout(w):
@@ -229,6 +306,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "exact_io_aware_25_amd", "csrc")
 KERNEL_SOURCE = os.path.join(CSRC, "attn_fwd.hip")
 KERNEL_SOURCE_BWD = os.path.join(CSRC, "attn_bwd.hip")
+KERNEL_SOURCE_DECODE = os.path.join(CSRC, "attn_decode.hip")
 
 
 def kernel_source_sha256(path: str = KERNEL_SOURCE) -> str:
@@ -280,11 +358,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default=None, choices=sorted(WORKLOADS) + sorted(DECODE_WORKLOADS))
     ap.add_argument("--sweep", action="store_true",
                     help="also time every workload and print one extra JSON line each (to stderr)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode", action="store_true",
+                    help="time the paged decode (attn_decode) on a decode workload")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (attn_bwd) on the workload instead of the forward")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -298,8 +378,11 @@ def main():
               "copies).", file=sys.stderr)
         sys.exit(2)
 
-    w = WORKLOADS[args.workload]
     attn.library()
+    if args.decode or args.workload in DECODE_WORKLOADS:
+        main_decode(DECODE_WORKLOADS[args.workload or DEFAULT_DECODE], args)
+        return
+    w = WORKLOADS[args.workload or DEFAULT_WORKLOAD]
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 2
         src = torch.ones(n, dtype=torch.float16, device="cuda:0")
@@ -363,6 +446,40 @@ def main():
                                            "slope_time": round(loglog_slope(Ls, ts), 3),
                                            "slope_memory": round(loglog_slope(Ls, ms_), 3)}}),
               file=sys.stderr, flush=True)
+
+
+def main_decode(w, args):
+    r = time_decode(w, args.steps, args.warmup)
+    nbytes = decode_bytes(w)
+    gbs = nbytes / (r["ms"] * 1e-3) / 1e9
+    lens = decode_lens(w)
+    line = {
+        "metric": METRIC_DECODE if w.name == DEFAULT_DECODE else f"paged decode GB/s ({w.name})",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: seeded iid N(0,1) q and KV cache rounded to the 16-bit type; seeded ragged "
+                "lengths and shuffled block tables",
+        "config": {"workload": w.name, "pass": "decode", "B": w.B, "H": w.H, "H_kv": w.H_kv, "d": w.d,
+                   "Lq": w.Lq, "block_size": w.block_size, "window": w.window, "scale": w.scale,
+                   "seq_len_min": min(lens), "seq_len_max": max(lens), "algorithmic_bytes": nbytes,
+                   "workspace_bytes": r["workspace_bytes"], "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                   "launches_per_step": 2},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": profiled_traffic(w, "attn_decode", KERNEL_SOURCE_DECODE),
+                     "scope": "one attn_decode call (partial and merge kernels)"},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_decode(w, r["out"], r["inputs"], args.cpu_budget)
+    print(json.dumps(line), flush=True)
 
 
 def main_backward(w, args):

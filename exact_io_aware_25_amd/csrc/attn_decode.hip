@@ -19,8 +19,8 @@
 //      transposing read of the second product), both one tile ahead; the
 //      online softmax is per lane; the chunk's (max, sum, unnormalised O)
 //      go to the workspace.
-//   2. merge: one wave per query row combines its chunks exactly (the same
-//      rescale the online softmax uses) and writes O and lse.
+//   2. merge: one workgroup per query row combines its chunks exactly (the
+//      same rescale the online softmax uses) and writes O and lse.
 // The products run on the 32x32x16 MFMA although at most Lq*H/H_kv of the
 // 32 query columns are live: the kernel is bound by bytes, not FLOPs.
 #include <hip/hip_runtime.h>
@@ -137,19 +137,30 @@ __global__ __launch_bounds__(64 * kDecWaves) void attn_decode_partial_kernel(Dec
         ld_v[cc] = row * kRowBytes + 16 * (phys ^ v_swizzle<D>(row));
     }
 
+    // The physical blocks of the two 16-key halves of tile t (wave-uniform).
+    // They are fetched two tiles ahead, so a tile's data loads never wait on
+    // a page-table load.
+    struct Pages { int lo, hi; };
+    auto pages_of = [&](int t) {
+        Pages pg;
+        pg.lo = (int)page_of(p, b, t * kDecTile);
+        pg.hi = (int)page_of(p, b, t * kDecTile + 16);
+        return pg;
+    };
     // K fragments of tile t into registers; V tile t into this wave's stage
-    auto load_k = [&](int t, vec8 (&kf)[kDSteps]) {
-        const int j = t * kDecTile + krow;
-        const T *row = kc + ((page_of(p, b, j) * p.H_kv + g) * p.bs + (j & (p.bs - 1))) * D;
+    auto load_k = [&](int t, Pages pg, vec8 (&kf)[kDSteps]) {
+        const int j = t * kDecTile + krow;  // krow < 16 exactly when l32 < 16
+        const int64_t page = l32 < 16 ? pg.lo : pg.hi;
+        const T *row = kc + ((page * p.H_kv + g) * p.bs + (j & (p.bs - 1))) * D;
 #pragma unroll
         for (int s = 0; s < kDSteps; ++s) kf[s] = *reinterpret_cast<const vec8 *>(row + 16 * s + 8 * hi);
     };
-    auto copy_v = [&](int t, char *stage) {
+    auto copy_v = [&](int t, Pages pg, char *stage) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             const int j0 = t * kDecTile + 16 * hf;
             const int valid = min(max(n - j0, 0), 16);  // rows past n arrive as zeros
-            const int64_t page = __builtin_amdgcn_readfirstlane((int)page_of(p, b, j0));
+            const int64_t page = __builtin_amdgcn_readfirstlane(hf ? pg.hi : pg.lo);
             const T *base = vc + ((page * p.H_kv + g) * p.bs + (j0 & (p.bs - 1))) * D;
             const __amdgpu_buffer_rsrc_t rv =
                 __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, valid * kRowBytes, 0x00020000);
@@ -229,22 +240,28 @@ __global__ __launch_bounds__(64 * kDecWaves) void attn_decode_partial_kernel(Dec
     // The wave waits for its own loads only (vmcnt); before a copy reuses a
     // stage, its reads of that stage have completed (lgkmcnt).
     vec8 kf_a[kDSteps], kf_b[kDSteps];
-    load_k(t_first, kf_a);
-    copy_v(t_first, stage_a);
+    Pages pg_next = pages_of(t_first + 1 < t_last ? t_first + 1 : t_first);
+    {
+        const Pages pg0 = pages_of(t_first);
+        load_k(t_first, pg0, kf_a);
+        copy_v(t_first, pg0, stage_a);
+    }
     for (int t = t_first; t < t_last; t += 2) {
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         if (t + 1 < t_last) {
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-            load_k(t + 1, kf_b);
-            copy_v(t + 1, stage_b);
+            load_k(t + 1, pg_next, kf_b);
+            copy_v(t + 1, pg_next, stage_b);
+            if (t + 2 < t_last) pg_next = pages_of(t + 2);
         }
         process(t, kf_a, stage_a);
         if (t + 1 < t_last) {
             __builtin_amdgcn_s_waitcnt(0x0F70);
             if (t + 2 < t_last) {
                 __builtin_amdgcn_s_waitcnt(0xC07F);
-                load_k(t + 2, kf_a);
-                copy_v(t + 2, stage_a);
+                load_k(t + 2, pg_next, kf_a);
+                copy_v(t + 2, pg_next, stage_a);
+                if (t + 3 < t_last) pg_next = pages_of(t + 3);
             }
             process(t + 1, kf_b, stage_b);
         }
@@ -272,34 +289,43 @@ __global__ __launch_bounds__(64 * kDecWaves) void attn_decode_partial_kernel(Dec
 }
 
 // ---------------------------------------------------------------- 2. merge
+// One workgroup of 4 waves per query row: every thread takes a share of the
+// chunks' maxima, the block agrees on the largest M, then wave w sums the
+// chunks c = w, w+4, ... with weights 2^(m_c - M) (lanes over d) and the
+// four partial sums meet in LDS.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_decode_merge_kernel(DecParams p)
 {
     constexpr int kPer = D / 64;  // elements of O per lane
+    __shared__ float red_m[4];
+    __shared__ float red_o[4][D + 1];
     const int wave = threadIdx.x / 64;
     const int lane = threadIdx.x % 64;
     const int64_t rows_total = (int64_t)p.B * p.H * p.Lq;
-    const int64_t row = (int64_t)blockIdx.x * 4 + wave;  // (b*H + h)*Lq + i
-    if (row >= rows_total) return;
+    const int64_t row = blockIdx.x;  // (b*H + h)*Lq + i
     const int b = (int)(row / ((int64_t)p.H * p.Lq));
     const int i = (int)(row % p.Lq);
     const int n = seq_len(p, b);
     const int pos = n - p.Lq + i;
     const int c_first = first_key(p, n) / p.chunk;
-    const int c_last = n > 0 ? (n - 1) / p.chunk : -1;
+    const int c_last = (pos >= 0 && n > 0) ? (n - 1) / p.chunk : c_first - 1;  // empty when pos < 0
     const float *pml = p.part + rows_total * p.n_chunks * D + 2 * row * p.n_chunks;
     const float *po = p.part + row * p.n_chunks * D;
 
     float m = -INFINITY;
-    if (pos >= 0)
-        for (int c = c_first + lane; c <= c_last; c += 64) m = fmaxf(m, pml[2 * c]);
+    for (int c = c_first + (int)threadIdx.x; c <= c_last; c += 256) m = fmaxf(m, pml[2 * c]);
 #pragma unroll
     for (int off = 32; off > 0; off /= 2) m = fmaxf(m, __shfl_xor(m, off));
+    if (lane == 0) red_m[wave] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+
     float l = 0.f, acc[kPer];
 #pragma unroll
     for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
     if (m != -INFINITY) {
-        for (int c = c_first; c <= c_last; ++c) {
+#pragma unroll 4
+        for (int c = c_first + wave; c <= c_last; c += 4) {
             const float mc = pml[2 * c];
             const float w = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - m);
             l += w * pml[2 * c + 1];
@@ -307,10 +333,20 @@ __global__ __launch_bounds__(256) void attn_decode_merge_kernel(DecParams p)
             for (int e = 0; e < kPer; ++e) acc[e] += w * po[(int64_t)c * D + e * 64 + lane];
         }
     }
-    T *orow = static_cast<T *>(p.o) + row * D;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) orow[e * 64 + lane] = (T)(acc[e] * inv);
+    for (int e = 0; e < kPer; ++e) red_o[wave][e * 64 + lane] = acc[e];
+    if (lane == 0) red_o[wave][D] = l;
+    __syncthreads();
+    if (wave != 0) return;
+    l = (red_o[0][D] + red_o[1][D]) + (red_o[2][D] + red_o[3][D]);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    T *orow = static_cast<T *>(p.o) + row * D;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+        const int d = e * 64 + lane;
+        const float o = (red_o[0][d] + red_o[1][d]) + (red_o[2][d] + red_o[3][d]);
+        orow[d] = (T)(o * inv);
+    }
     if (lane == 0) p.lse[row] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
 }
 
@@ -345,7 +381,7 @@ hipError_t launch_decode(DecParams p, hipStream_t stream)
     if (err != hipSuccess) return err;
     const int64_t rows_total = (int64_t)p.B * p.H * p.Lq;
     return hipLaunchKernel(reinterpret_cast<const void *>(&attn_decode_merge_kernel<T, D>),
-                           dim3((unsigned)((rows_total + 3) / 4)), dim3(256), kargs, 0, stream);
+                           dim3((unsigned)rows_total), dim3(256), kargs, 0, stream);
 }
 
 template <typename T>
@@ -382,7 +418,7 @@ int attn_decode_impl(const void *q, const void *k_cache, const void *v_cache, co
     const int chunk = decode_chunk(B, H_kv, n_rowblk, max_seq_len);
     const int n_chunks = (max_seq_len + chunk - 1) / chunk;
     const int n_cgroups = (n_chunks + kDecWaves - 1) / kDecWaves;
-    if ((int64_t)B * H_kv * n_rowblk * n_cgroups > INT_MAX || (int64_t)B * H * Lq / 4 + 1 > INT_MAX)
+    if ((int64_t)B * H_kv * n_rowblk * n_cgroups > INT_MAX || (int64_t)B * H * Lq > INT_MAX)
         return ATTN_ERR_SIZE;
 
     const size_t bytes_q = (size_t)(q_elems * sizeof(T));

@@ -379,10 +379,6 @@ def main():
         sys.exit(2)
 
     attn.library()
-    if args.decode or args.workload in DECODE_WORKLOADS:
-        main_decode(DECODE_WORKLOADS[args.workload or DEFAULT_DECODE], args)
-        return
-    w = WORKLOADS[args.workload or DEFAULT_WORKLOAD]
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 2
         src = torch.ones(n, dtype=torch.float16, device="cuda:0")
@@ -391,6 +387,10 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.decode or args.workload in DECODE_WORKLOADS:
+        main_decode(DECODE_WORKLOADS[args.workload or DEFAULT_DECODE], args)
+        return
+    w = WORKLOADS[args.workload or DEFAULT_WORKLOAD]
     if args.backward:
         main_backward(w, args)
         return

@@ -34,7 +34,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(_HERE, "attn_oracle.c")
 LIBRARY = os.path.join(_HERE, "_attn_oracle.so")
 
-DTYPES = {"f16": 0, "fp16": 0, "float16": 0, "bf16": 1, "bfloat16": 1}
+DTYPES = {"f16": 0, "fp16": 0, "float16": 0, "bf16": 1, "bfloat16": 1, "f8": 2, "f8e4m3": 2}
 
 _lib = None
 
@@ -73,6 +73,8 @@ def _bind(lib):
                                     f64p, f64p, f64p, f64p, f64p, f64p, f64p, f64p, ctypes.c_int]
     lib.oracle_decode.restype = None
     lib.oracle_decode.argtypes = [u16p, f64p, ctypes.c_int64, ctypes.c_int]
+    lib.oracle_f8e4m3_to_f64.restype = ctypes.c_double
+    lib.oracle_f8e4m3_to_f64.argtypes = [ctypes.c_uint16]
     lib.oracle_resolve_scale.restype = ctypes.c_float
     lib.oracle_resolve_scale.argtypes = [ctypes.c_float, ctypes.c_int]
     lib.oracle_visible.restype = ctypes.c_int
@@ -97,10 +99,15 @@ def _ptr(a, ctype):
 
 
 def _bits(a) -> np.ndarray:
-    """16-bit patterns of a float16/bfloat16 torch tensor or a uint16/float16 array."""
+    """16-bit patterns of a float16/bfloat16 torch tensor or a uint16/float16
+    array; an fp8 (float8_e4m3fn) tensor or uint8 array gives its bytes
+    widened to uint16 (the oracle's "f8" dtype reads the low byte)."""
     if hasattr(a, "detach"):  # torch tensor, CPU
         import torch
-        a = a.detach().cpu().contiguous().view(torch.int16).numpy()
+        a = a.detach().cpu().contiguous()
+        a = a.view(torch.uint8).numpy() if a.element_size() == 1 else a.view(torch.int16).numpy()
+    if isinstance(a, np.ndarray) and a.dtype == np.uint8:
+        return np.ascontiguousarray(a).astype(np.uint16)
     a = np.ascontiguousarray(a)
     if a.dtype == np.float16:
         a = a.view(np.uint16)

@@ -28,8 +28,9 @@
  *   O[i,:] = sum_j exp(s_ij - m_i) * v[b,g,j,:] / l_i
  *   lse_i  = m_i + ln(l_i)                        (natural-log logsumexp)
  *
- * Inputs are 16-bit float bit patterns (IEEE binary16 or bfloat16), decoded
- * exactly to double.  The scale is the fp32 value the GPU receives, widened.
+ * Inputs are 16-bit float bit patterns (IEEE binary16 or bfloat16), or OCP
+ * fp8 E4M3 patterns in the low byte of 16-bit words, decoded exactly to
+ * double.  The scale is the fp32 value the GPU receives, widened.
  * Outputs are fp64 and are not rounded.
  *
  * Readings of points the pages leave open (each one also listed in the
@@ -44,7 +45,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORACLE_F16 = 0, ORACLE_BF16 = 1 };
+enum { ORACLE_F16 = 0, ORACLE_BF16 = 1, ORACLE_F8E4M3 = 2 };
 
 /* IEEE-754 binary16: sign bit, 5-bit exponent with bias 15, 10-bit fraction.
  * Exponent 0 encodes zero/subnormals (fraction * 2^-24), exponent 31 encodes
@@ -73,8 +74,30 @@ double oracle_bf16_to_f64(uint16_t bits)
     return (double)f;
 }
 
+/* OCP FP8 E4M3 ("e4m3fn", the float8_e4m3fn type of «Оптимизация внимания
+ * Flash», Workflow 3, Step 3): sign bit, 4-bit exponent with bias 7, 3-bit
+ * fraction.  Exponent 0 encodes zero/subnormals (fraction * 2^-9); there are
+ * no infinities, and S.1111.111 is NaN (the largest finite value is 448).
+ * The byte is the low 8 bits of `bits`. */
+double oracle_f8e4m3_to_f64(uint16_t bits)
+{
+    int sign = (bits >> 7) & 1;
+    int expo = (bits >> 3) & 0xf;
+    int frac = bits & 0x7;
+    double mag;
+    if (expo == 0)
+        mag = ldexp((double)frac, -9);
+    else if (expo == 15 && frac == 7)
+        mag = NAN;
+    else
+        mag = ldexp((double)(8 + frac), expo - 10); /* 1.frac * 2^(expo-7) */
+    return sign ? -mag : mag;
+}
+
 static double decode(uint16_t bits, int dtype)
 {
+    if (dtype == ORACLE_F8E4M3)
+        return oracle_f8e4m3_to_f64(bits);
     return dtype == ORACLE_BF16 ? oracle_bf16_to_f64(bits) : oracle_f16_to_f64(bits);
 }
 

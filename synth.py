@@ -9,8 +9,10 @@ standard-normal draws («ТЕХНИЧЕСКОЕ ЗАДАНИЕ: Сравнить
 на 128k», stage 2, the FlashAttention benchmark function; «Оптимизация
 внимания Flash», Quick start and Workflow 1, Steps 3-4).  Here q, then k, then
 v are drawn as fp32 N(0,1) from one CPU generator seeded with `seed`, then
-rounded to the 16-bit type (round to nearest even).  The same bits go to the
-GPU and to the oracle.
+rounded to the input type (round to nearest even; fp8 inputs are drawn the
+same way and cast to float8_e4m3fn, as «Оптимизация внимания Flash»,
+Workflow 3, Step 3 casts its fp16 inputs).  The same bits go to the GPU and
+to the oracle.
 """
 from __future__ import annotations
 
@@ -18,7 +20,7 @@ import dataclasses
 
 import torch
 
-TORCH_DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16}
+TORCH_DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16, "f8": torch.float8_e4m3fn}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -29,7 +31,7 @@ class Workload:
     H_kv: int
     L: int
     d: int
-    dtype: str          # "f16" or "bf16"
+    dtype: str          # "f16", "bf16" or "f8" (OCP fp8 E4M3 inputs, bf16 output)
     causal: bool
     window: int         # -1: no window; else keys at most `window` before (and, non-causal, after)
     scale: float        # the fp32 softmax scale passed to the library
@@ -53,6 +55,10 @@ class Workload:
 #   p2_accuracy:  «Оптимизация внимания Flash», Workflow 1, Step 4 (accuracy check):
 #                 batch 1, 8 heads, 512 tokens, head_dim 64, scale 1/8, no mask,
 #                 fp16, max difference below 1e-3.
+#   fp8_fa3_4k:   «Оптимизация внимания Flash», Workflow 3, Steps 3-4: fp16 randn
+#                 inputs of [batch 2, 4096 tokens, 32 heads, head_dim 64] cast to
+#                 float8_e4m3fn, default scale, no mask.
+#   fp8_causal_128k_h4: the headline shape with fp8 inputs.
 _INV_SQRT_128 = float(torch.tensor(1.0 / 128 ** 0.5, dtype=torch.float32))
 
 WORKLOADS = {
@@ -68,6 +74,8 @@ WORKLOADS = {
         Workload("causal_128k_h8", 1, 8, 8, 131072, 64, "f16", True, -1, 0.125, 1003),
         Workload("swa_gqa_16k", 1, 32, 8, 16384, 128, "bf16", True, 4096, _INV_SQRT_128, 1004),
         Workload("p2_accuracy", 1, 8, 8, 512, 64, "f16", False, -1, 0.125, 1005),
+        Workload("fp8_fa3_4k", 2, 32, 32, 4096, 64, "f8", False, -1, 0.125, 1006),
+        Workload("fp8_causal_128k_h4", 1, 4, 4, 131072, 64, "f8", True, -1, 0.125, 1003),
     ]
 }
 

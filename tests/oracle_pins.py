@@ -54,6 +54,32 @@ def pin_decoders_exhaustive(lib):
     assert np.array_equal(got[~nan], want[~nan]), "bf16 values"
 
 
+def pin_f8_decoder_exhaustive(lib):
+    """OCP fp8 E4M3 (float8_e4m3fn): all 256 patterns against torch's own
+    conversion (values, the two NaN patterns, signed zero)."""
+    bits = np.arange(256, dtype=np.uint8)
+    got = oracle.decode(bits, "f8", lib=lib)
+    want = torch.from_numpy(bits).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan), "fp8 NaN patterns"
+    assert np.array_equal(got[~nan], want[~nan]), "fp8 values"
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan])), "fp8 signed zeros"
+
+
+def pin_f8_inputs_equal_their_f16_widening(lib):
+    """Every fp8 E4M3 value is exactly a binary16 value, so attention of fp8
+    inputs equals attention of the same values widened to fp16 (bitwise), and
+    matches the NumPy brute force."""
+    for (L, H, H_kv, causal, window, seed) in [(40, 4, 2, True, -1, 51), (33, 2, 2, False, 5, 52)]:
+        q, k, v = make_qkv(1, H, H_kv, L, 64, "f8", seed)
+        o8, l8 = _run(lib, q, k, v, "f8", causal, window, 0.125)
+        o16, l16 = _run(lib, q.to(torch.float16), k.to(torch.float16), v.to(torch.float16), "f16", causal,
+                        window, 0.125)
+        assert np.array_equal(o8, o16) and np.array_equal(l8, l16)
+        bo, bl = brute.attention(_f64(q), _f64(k), _f64(v), causal, window, 0.125)
+        assert np.max(np.abs(o8 - bo)) <= 1e-12 and np.max(np.abs(l8 - bl)) <= 1e-12
+
+
 # ---------------------------------------------------------------- brute force
 BRUTE_GRID_FULL = dict(L=[1, 2, 3, 7, 17, 64, 130], d=[64, 128], heads=[(1, 1), (4, 2), (4, 1)],
                        causal=[False, True], window=[-1, 0, 1, 5], dtype=["f16", "bf16"])
@@ -292,7 +318,7 @@ def pin_row_subset(lib):
 
 
 ALL_PINS = [
-    pin_decoders_exhaustive, pin_brute_force, pin_torch_sdpa, pin_single_visible_key,
+    pin_decoders_exhaustive, pin_f8_decoder_exhaustive, pin_f8_inputs_equal_their_f16_widening, pin_brute_force, pin_torch_sdpa, pin_single_visible_key,
     pin_causal_row0, pin_zero_keys, pin_identical_values, pin_ones, pin_two_keys,
     pin_key_shift, pin_permutation, pin_scale_vs_query, pin_gqa_equals_repeated_heads,
     pin_batch_independence, pin_default_scale, pin_row_subset,

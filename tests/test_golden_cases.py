@@ -30,6 +30,8 @@ def test_workloads_follow_the_pages():
                    if w.causal and w.window < 0 and w.d == sweep["d"] and w.B == sweep["B"])
     assert sorted(set(swept)) == sweep["lengths"]
     assert {w.H for w in WORKLOADS.values() if w.L == 131072} == set(sweep["H"])
+    fp8 = GOLDEN["p2_fp8_shape"]
+    assert _shape(WORKLOADS["fp8_fa3_4k"]) == {k: fp8[k] for k in _shape(WORKLOADS["fp8_fa3_4k"])}
 
 
 def test_oracle_meets_page_accuracy_bound(oracle_lib):

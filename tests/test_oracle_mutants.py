@@ -29,6 +29,9 @@ MUTANTS = {
     "default_scale_wrong": ("return (float)(1.0 / sqrt((double)d));", "return (float)(1.0 / (double)d);"),
     "max_not_subtracted_from_lse_side": ("double p = exp(s[j] - m);", "double p = exp(s[j]);"),
     "sum_over_one_row_only": ("l += p;", "l = p;"),
+    "f8_bias": ("mag = ldexp((double)(8 + frac), expo - 10);", "mag = ldexp((double)(8 + frac), expo - 9);"),
+    "f8_subnormal_exponent": ("mag = ldexp((double)frac, -9);", "mag = ldexp((double)frac, -10);"),
+    "f8_top_exponent_is_nan": ("else if (expo == 15 && frac == 7)", "else if (expo == 15)"),
     # backward pass
     "bwd_dq_uses_values": ("acc[c] += dS * kd[j * d + c];", "acc[c] += dS * vd[j * d + c];"),
     "bwd_dq_scale_dropped": ("dq[t * d + c] = sc * acc[c];", "dq[t * d + c] = acc[c];"),

@@ -47,6 +47,12 @@ import exact_io_aware_25_amd as attn  # noqa: E402
 from synth import DECODE_WORKLOADS, WORKLOADS, decode_inputs, decode_lens, workload_inputs  # noqa: E402
 
 MFMA_PEAK_F16_TFLOPS = 2516.6   # MI355X dense fp16/bf16: 256 CU x 4096 FLOP/clk x 2.4 GHz
+MFMA_PEAK_F8_TFLOPS = 5033.2    # MI355X dense fp8: twice the 16-bit rate
+
+
+def mfma_peak(w) -> float:
+    """The dense MFMA peak of the workload's input type."""
+    return MFMA_PEAK_F8_TFLOPS if w.dtype == "f8" else MFMA_PEAK_F16_TFLOPS
 HBM_PEAK_GBS = 8000.0
 METRIC = "causal attn fwd TFLOP/s @ L=128k,H=4,d=64 fp16; % of MFMA peak"
 METRIC_BWD = "causal attn bwd TFLOP/s @ L=128k,H=4,d=64 fp16; % of MFMA peak"
@@ -91,8 +97,11 @@ def algorithmic_bytes_bwd(w) -> float:
 
 
 def algorithmic_bytes(w) -> float:
-    """One read of q, k, v and one write of out (16-bit) and lse (fp32)."""
-    return 2.0 * w.B * w.L * w.d * (2 * w.H + 2 * w.H_kv) + 4.0 * w.B * w.H * w.L
+    """One read of q, k, v and one write of out and lse (fp32): 2 bytes per
+    element for 16-bit inputs; fp8 inputs are 1 byte and their output bf16."""
+    inp = 1.0 if w.dtype == "f8" else 2.0
+    return (inp * w.B * w.L * w.d * (w.H + 2 * w.H_kv) + 2.0 * w.B * w.L * w.d * w.H
+            + 4.0 * w.B * w.H * w.L)
 
 
 def time_workload(w, steps: int, warmup: int):
@@ -105,7 +114,7 @@ def time_workload(w, steps: int, warmup: int):
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats(dev)
     base = torch.cuda.memory_allocated(dev)
-    out = torch.empty_like(q)
+    out = torch.empty(q.shape, dtype=torch.bfloat16 if w.dtype == "f8" else q.dtype, device=dev)
     lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     for _ in range(warmup):
@@ -313,6 +322,7 @@ CSRC = os.path.join(ROOT, "exact_io_aware_25_amd", "csrc")
 KERNEL_SOURCE = os.path.join(CSRC, "attn_fwd.hip")
 KERNEL_SOURCE_BWD = os.path.join(CSRC, "attn_bwd.hip")
 KERNEL_SOURCE_DECODE = os.path.join(CSRC, "attn_decode.hip")
+KERNEL_SOURCE_F8 = os.path.join(CSRC, "attn_fwd_f8.hip")
 
 
 def kernel_source_sha256(path: str = KERNEL_SOURCE) -> str:
@@ -349,9 +359,11 @@ def profiled_traffic(w, kind: str = "attn_fwd", source: str = KERNEL_SOURCE):
 def roofline_block(w, ms):
     flops = algorithmic_flops(w)
     achieved = flops / (ms * 1e-3) / 1e12
-    return {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_PEAK_F16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_F16_TFLOPS, 4),
-            "traffic": profiled_traffic(w)}
+    peak = mfma_peak(w)
+    source = KERNEL_SOURCE_F8 if w.dtype == "f8" else KERNEL_SOURCE
+    return {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+            "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+            "traffic": profiled_traffic(w, "attn_fwd", source)}
 
 
 def loglog_slope(xs, ys):
@@ -409,7 +421,7 @@ def main():
     flops = algorithmic_flops(w)
     tflops = flops / (r["ms"] * 1e-3) / 1e12
     line = {
-        "metric": METRIC,
+        "metric": METRIC if w.name == DEFAULT_WORKLOAD else f"attn fwd TFLOP/s ({w.name})",
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -420,10 +432,10 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic: seeded iid N(0,1) q, k, v rounded to the 16-bit type",
+        "data": "synthetic: seeded iid N(0,1) q, k, v rounded to the input type",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.H_kv, "L": w.L, "d": w.d,
                    "causal": w.causal, "window": w.window, "scale": w.scale,
-                   "algorithmic_flops": flops, "pct_of_mfma_peak": round(100 * tflops / MFMA_PEAK_F16_TFLOPS, 2),
+                   "algorithmic_flops": flops, "pct_of_mfma_peak": round(100 * tflops / mfma_peak(w), 2),
                    "peak_mem_bytes": r["peak_mem"], "peak_mem_call_bytes": r["peak_mem_call"],
                    "algorithmic_bytes": algorithmic_bytes(w)},
         "roofline": roofline_block(w, r["ms"]),
@@ -439,9 +451,9 @@ def main():
         for name, ws in WORKLOADS.items():
             rs = time_workload(ws, max(5, args.steps), 3)
             f = algorithmic_flops(ws)
-            rec = {"workload": name, "L": ws.L, "ms": round(rs["ms"], 4),
+            rec = {"workload": name, "dtype": ws.dtype, "L": ws.L, "ms": round(rs["ms"], 4),
                    "tflops": round(f / (rs["ms"] * 1e-3) / 1e12, 2),
-                   "pct_peak": round(100 * f / (rs["ms"] * 1e-3) / 1e12 / MFMA_PEAK_F16_TFLOPS, 2),
+                   "pct_peak": round(100 * f / (rs["ms"] * 1e-3) / 1e12 / mfma_peak(ws), 2),
                    "peak_mem_bytes": rs["peak_mem"], "peak_mem_call_bytes": rs["peak_mem_call"],
                    "algorithmic_bytes": algorithmic_bytes(ws)}
             sweep.append(rec)

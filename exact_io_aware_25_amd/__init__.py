@@ -29,7 +29,7 @@ ATTN_ERR_FLAG = 8
 ATTN_ERR_SCALE = 9
 ATTN_ERR_ALIGN = 10
 
-EXPORTS = ("attn_fwd", "attn_fwd_bf16", "attn_bwd", "attn_bwd_bf16", "attn_bwd_workspace_size",
+EXPORTS = ("attn_fwd", "attn_fwd_bf16", "attn_fwd_fp8", "attn_bwd", "attn_bwd_bf16", "attn_bwd_workspace_size",
            "attn_decode", "attn_decode_bf16", "attn_decode_workspace_size",
            "attn_launch_shape", "attn_status_string", "attn_resolve_scale")
 
@@ -55,7 +55,7 @@ def library():
         sig = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                ctypes.c_int, ctypes.c_int, ctypes.c_float, ctypes.c_void_p]
-        for name in ("attn_fwd", "attn_fwd_bf16"):
+        for name in ("attn_fwd", "attn_fwd_bf16", "attn_fwd_fp8"):
             fn = getattr(lib, name)
             fn.restype = ctypes.c_int
             fn.argtypes = sig
@@ -130,6 +130,11 @@ def attn_decode_workspace_size(B, H, H_kv, Lq, d, max_seq_len) -> int:
     return int(library().attn_decode_workspace_size(int(B), int(H), int(H_kv), int(Lq), int(d), int(max_seq_len)))
 
 
+def attn_fwd_fp8(q, k, v, out, lse, B, H, H_kv, L, d, causal, window, scale, stream) -> int:
+    """fp8 (E4M3) entry point; out is bf16."""
+    return library().attn_fwd_fp8(q, k, v, out, lse, B, H, H_kv, L, d, causal, window, scale, stream)
+
+
 def attn_status_string(status: int) -> str:
     return library().attn_status_string(int(status)).decode()
 
@@ -149,9 +154,10 @@ def attn_launch_shape(B, H, L, d, causal, window):
 
 def forward(q, k, v, causal: bool = False, window: int = -1, scale=None, out=None, lse=None,
             stream=None):
-    """Attention of torch tensors q [B,H,L,d], k and v [B,H_kv,L,d] (fp16 or bf16, on the GPU).
+    """Attention of torch tensors q [B,H,L,d], k and v [B,H_kv,L,d] (fp16, bf16 or
+    float8_e4m3fn, on the GPU).
 
-    Returns (out [B,H,L,d] of q's dtype, lse [B,H,L] fp32).  ``scale=None``
+    Returns (out [B,H,L,d] of q's dtype -- bf16 for fp8 inputs --, lse [B,H,L] fp32).  ``scale=None``
     selects 1/sqrt(d).  ``out``/``lse`` may be given to write into existing
     tensors.  Launches on ``stream`` (default: torch's current stream).
     """
@@ -159,8 +165,10 @@ def forward(q, k, v, causal: bool = False, window: int = -1, scale=None, out=Non
 
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D: [B, H, L, d] and [B, H_kv, L, d]")
-    if q.dtype not in (torch.float16, torch.bfloat16) or k.dtype != q.dtype or v.dtype != q.dtype:
-        raise ValueError("q, k, v must share one dtype, float16 or bfloat16")
+    if (q.dtype not in (torch.float16, torch.bfloat16, torch.float8_e4m3fn) or k.dtype != q.dtype
+            or v.dtype != q.dtype):
+        raise ValueError("q, k, v must share one dtype: float16, bfloat16 or float8_e4m3fn")
+    out_dtype = torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
     if not (q.is_cuda and k.device == q.device and v.device == q.device):
         raise ValueError("q, k, v must be on the same GPU device")
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
@@ -170,18 +178,18 @@ def forward(q, k, v, causal: bool = False, window: int = -1, scale=None, out=Non
     if tuple(k.shape) != (B, H_kv, L, d) or tuple(v.shape) != tuple(k.shape):
         raise ValueError(f"shape mismatch: q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, L), dtype=torch.float32, device=q.device)
-    if (tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or not out.is_contiguous()
+    if (tuple(out.shape) != tuple(q.shape) or out.dtype != out_dtype or not out.is_contiguous()
             or out.device != q.device):
-        raise ValueError("out must be a contiguous tensor like q")
+        raise ValueError("out must be a contiguous tensor shaped like q (bf16 for fp8 inputs)")
     if (tuple(lse.shape) != (B, H, L) or lse.dtype != torch.float32 or not lse.is_contiguous()
             or lse.device != q.device):
         raise ValueError("lse must be a contiguous float32 tensor [B, H, L]")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    fn = attn_fwd if q.dtype == torch.float16 else attn_fwd_bf16
+    fn = {torch.float16: attn_fwd, torch.bfloat16: attn_fwd_bf16, torch.float8_e4m3fn: attn_fwd_fp8}[q.dtype]
     with torch.cuda.device(q.device):
         status = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                     B, H, H_kv, L, d, int(bool(causal)), int(window),

@@ -6,7 +6,7 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", name) for name in ("attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip")]
+SOURCES = [os.path.join(PKG, "csrc", name) for name in ("attn_fwd.hip", "attn_fwd_f8.hip", "attn_bwd.hip", "attn_decode.hip")]
 LIBRARY = os.path.join(PKG, "libattn_gfx950.so")
 CALIBRATE_SOURCE = os.path.join(PKG, "csrc", "calibrate_gfx950.hip")
 CALIBRATE = os.path.join(PKG, "calibrate_gfx950")

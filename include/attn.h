@@ -92,6 +92,19 @@ int attn_fwd_bf16(const void *q, const void *k, const void *v, void *out, float 
                   int B, int H, int H_kv, int L, int d, int causal, int window, float scale,
                   void *stream);
 
+/*
+ * The same forward pass for fp8 inputs: q, k, v hold OCP FP8 E4M3 bytes
+ * (float8_e4m3fn, as «Оптимизация внимания Flash», Workflow 3, Step 3 casts
+ * them), same layouts; out is bf16 [B, H, L, d]; lse fp32.  The result is
+ * the definition above of the decoded inputs; both products run on the fp8
+ * MFMA, so the softmax weights enter the second product rounded to E4M3
+ * (the row sums, and so lse, stay fp32).  Same argument rules as attn_fwd;
+ * q, k, v, out 16-byte aligned.
+ */
+int attn_fwd_fp8(const void *q, const void *k, const void *v, void *out, float *lse,
+                 int B, int H, int H_kv, int L, int d, int causal, int window, float scale,
+                 void *stream);
+
 /* A static, human-readable name for a status code (never NULL). */
 const char *attn_status_string(int status);
 

@@ -58,6 +58,7 @@ class Workload:
 #   fp8_fa3_4k:   «Оптимизация внимания Flash», Workflow 3, Steps 3-4: fp16 randn
 #                 inputs of [batch 2, 4096 tokens, 32 heads, head_dim 64] cast to
 #                 float8_e4m3fn, default scale, no mask.
+#   fa3_4k_f16:   the same shape and draws in fp16 (the page's fp16 reference).
 #   fp8_causal_128k_h4: the headline shape with fp8 inputs.
 _INV_SQRT_128 = float(torch.tensor(1.0 / 128 ** 0.5, dtype=torch.float32))
 
@@ -75,6 +76,7 @@ WORKLOADS = {
         Workload("swa_gqa_16k", 1, 32, 8, 16384, 128, "bf16", True, 4096, _INV_SQRT_128, 1004),
         Workload("p2_accuracy", 1, 8, 8, 512, 64, "f16", False, -1, 0.125, 1005),
         Workload("fp8_fa3_4k", 2, 32, 32, 4096, 64, "f8", False, -1, 0.125, 1006),
+        Workload("fa3_4k_f16", 2, 32, 32, 4096, 64, "f16", False, -1, 0.125, 1006),
         Workload("fp8_causal_128k_h4", 1, 4, 4, 131072, 64, "f8", True, -1, 0.125, 1003),
     ]
 }

@@ -46,7 +46,7 @@ def call(fn=attn.attn_fwd, q=Q, k=K, v=V, o=O, lse=LSE, B=1, H=4, H_kv=2, L=256,
     return fn(q, k, v, o, lse, B, H, H_kv, L, d, causal, window, scale, None)
 
 
-@pytest.mark.parametrize("fn", [attn.attn_fwd, attn.attn_fwd_bf16])
+@pytest.mark.parametrize("fn", [attn.attn_fwd, attn.attn_fwd_bf16, attn.attn_fwd_fp8])
 def test_argument_errors(fn):
     assert call(fn, q=0) == attn.ATTN_ERR_NULL
     assert call(fn, lse=0) == attn.ATTN_ERR_NULL
@@ -72,7 +72,7 @@ def test_argument_errors(fn):
     assert call(fn, lse=LSE + 2) == attn.ATTN_ERR_ALIGN
 
 
-@pytest.mark.parametrize("fn", [attn.attn_fwd, attn.attn_fwd_bf16])
+@pytest.mark.parametrize("fn", [attn.attn_fwd, attn.attn_fwd_bf16, attn.attn_fwd_fp8])
 def test_empty_problems_return_ok_without_launching(fn):
     assert call(fn, q=0, k=0, v=0, o=0, lse=0, B=0) == attn.ATTN_OK
     assert call(fn, q=0, k=0, v=0, o=0, lse=0, L=0) == attn.ATTN_OK
@@ -90,7 +90,7 @@ def test_binding_does_not_import_the_oracle():
     import sys
     src = open(os.path.join(ROOT, "exact_io_aware_25_amd", "__init__.py")).read()
     assert "oracle" not in src.replace("no fallback", "")
-    for name in ("attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip", "attn_common.h"):
+    for name in ("attn_fwd.hip", "attn_fwd_f8.hip", "attn_bwd.hip", "attn_decode.hip", "attn_common.h"):
         hip = open(os.path.join(ROOT, "exact_io_aware_25_amd", "csrc", name)).read()
         assert "oracle" not in hip, name
 

@@ -1,0 +1,100 @@
+"""GPU parity of the fp8 (OCP E4M3) forward against the fp64 oracle.
+
+The inputs are exact fp8 values (the oracle decodes them exactly); the kernel
+rounds each softmax weight to E4M3 before the second product (unit roundoff
+u = 2^-4) and writes O in bf16.  Tolerance, derived from that arithmetic:
+rounding a weight w to E4M3 changes it by a relative error that is uniform in
+[-u, u] (std u/sqrt(3)); independent over keys, so the error of O_ic is a
+random sum with standard deviation (u/sqrt(3)) * R_ic, where
+R_ic = sqrt(sum_j P_ij^2 v_jc^2).  The bound per element is the bf16 rounding
+floor of the exact value plus six standard deviations, plus 2^-12 for weights
+in E4M3's subnormal range (absolute steps of 2^-9 against a largest weight of
+8).  lse comes from fp32 sums of the unrounded weights: the forward's 1e-3.
+
+R is obtained from the oracle itself: sum_j P_ij^2 v_jc^2 =
+exp(lse2_i - 2 lse_i) * O2_ic, where (O2, lse2) is attention with the scores
+doubled (scale 2s) and the values squared (v^2 of an E4M3 value is exact in
+fp16, as are the E4M3 inputs widened to fp16).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_io_aware_25_amd as attn
+import oracle
+from synth import WORKLOADS, make_qkv, sample_rows, workload_inputs
+from test_gpu_parity import LSE_TOL, announce
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+U8 = 2.0 ** -4
+
+
+def fp8_bound_inputs(q, k, v, causal, window, scale, rows=None):
+    """Oracle O, lse and the per-element R of the fp8 inputs (rows optional)."""
+    q16, k16, v16 = (t.to(torch.float16) for t in (q, k, v))
+    o, lse = oracle.attention(q16, k16, v16, "f16", causal, window, scale, rows=rows)
+    o2, lse2 = oracle.attention(q16, k16, v16 * v16, "f16", causal, window, 2 * scale, rows=rows)
+    r = np.sqrt(np.maximum(o2, 0.0) * np.exp(lse2 - 2 * lse)[..., None])
+    return o, lse, r
+
+
+def check_fp8(out, lse, ref_o, ref_lse, r, case):
+    o = out.double().numpy().reshape(ref_o.shape)
+    l = lse.double().numpy().reshape(ref_lse.shape)
+    assert np.isfinite(o).all() and np.isfinite(l).all(), f"{case}: non-finite output"
+    floor = np.abs(torch.from_numpy(ref_o).to(torch.bfloat16).double().numpy() - ref_o)
+    bound = floor + 6 * (U8 / math.sqrt(3)) * r + 2.0 ** -12
+    err = np.abs(o - ref_o)
+    worst = np.unravel_index(np.argmax(err - bound), err.shape)
+    assert (err <= bound).all(), (f"{case}: error {err[worst]:.3e} > bound {bound[worst]:.3e} at {worst} "
+                                  f"(exact {ref_o[worst]:.4e}, R {r[worst]:.3e})")
+    lerr = float(np.abs(l - ref_lse).max())
+    assert lerr <= LSE_TOL, f"{case}: max|dlse| = {lerr:.3e}"
+    print(f"  {case}: max|dO| {err.max():.3e}, max error/bound {(err / bound).max():.3f}, max|dlse| {lerr:.2e}",
+          flush=True)
+    return float(err.max()), float((err / bound).max())
+
+
+GRID_L = [1, 2, 17, 64, 65, 129, 300]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_small_grid(d, causal):
+    seed = 500 + d + int(causal)
+    for L in GRID_L:
+        for window in (-1, 0, 37):
+            for H, H_kv in ((4, 2), (2, 2)):
+                seed += 1
+                case = f"fp8 H={H}/{H_kv} L={L} d={d} causal={causal} window={window}"
+                announce(case)
+                q, k, v = make_qkv(1, H, H_kv, L, d, "f8", seed)
+                out, lse = attn.forward(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, window=window)
+                torch.cuda.synchronize()
+                scale = oracle.resolve_scale(0.0, d)
+                ref_o, ref_l, r = fp8_bound_inputs(q, k, v, causal, window, scale)
+                check_fp8(out.cpu(), lse.cpu(), ref_o, ref_l, r, case)
+
+
+@pytest.mark.parametrize("name", ["fp8_fa3_4k", "fp8_causal_128k_h4"])
+def test_fp8_workload_sampled(name):
+    w = WORKLOADS[name]
+    announce(f"fp8 workload {name}")
+    q, k, v = workload_inputs(w)
+    out, lse = attn.forward(q.to(DEV), k.to(DEV), v.to(DEV), causal=w.causal, window=w.window, scale=w.scale)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.B, w.H, w.L, 24, seed=17)
+    ref_o, ref_l, r = fp8_bound_inputs(q, k, v, w.causal, w.window, w.scale, rows=rows)
+    check_fp8(out.cpu().reshape(-1, w.d)[rows], lse.cpu().reshape(-1)[rows], ref_o, ref_l, r, name)
+
+
+def test_fp8_single_key_is_exact():
+    """window = 0: the one weight is exactly 8 (representable), so O is V rounded to bf16 (exact)."""
+    q, k, v = make_qkv(1, 2, 2, 100, 64, "f8", 77)
+    out, _ = attn.forward(q.to(DEV), k.to(DEV), v.to(DEV), causal=True, window=0)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), v.to(torch.bfloat16))

@@ -119,7 +119,8 @@ def test_small_grid(dtype, d, causal):
 FULL_ORACLE = {"causal_4k", "noncausal_2k_f16", "noncausal_2k_bf16", "p2_accuracy"}
 
 
-@pytest.mark.parametrize("name", sorted(WORKLOADS))
+# fp8 workloads have a bound of their own (weights rounded to E4M3): test_gpu_fp8.py
+@pytest.mark.parametrize("name", sorted(n for n, w in WORKLOADS.items() if w.dtype != "f8"))
 def test_workload(name):
     w = WORKLOADS[name]
     announce(f"workload {name}: B={w.B} H={w.H}/{w.H_kv} L={w.L} d={w.d} {w.dtype} "

@@ -10,7 +10,13 @@
 //         read from lane i's own offset, and out-of-range lanes write zeros.
 //   calibrate_gfx950 --rates   issue rates per SIMD, no memory traffic:
 //       MFMA 32x32x16 f16 alone, the softmax VALU mix of one 64-key tile
-//       alone, both in one wave, and one MFMA wave beside one VALU wave.
+//       alone, both in one wave, and one MFMA wave beside one VALU wave;
+//       then the cost of single instructions (8 independent chains per
+//       wave) with 1 and 4 waves per SIMD, and 4 MFMAs with 16 independent
+//       FMAs of the same wave between them.
+//   calibrate_gfx950 --read    HBM read rate of a plain kernel over 3.3 GB,
+//       the data read in 4 KiB blocks in order and in a random order (the
+//       access pattern of a paged KV cache).
 //
 // Every memory access stays inside the buffers it is given.
 #include <hip/hip_runtime.h>
@@ -224,6 +230,73 @@ static int time_mode(const char *name, int waves_per_simd, int cus, float *out, 
     return 0;
 }
 
+// ------------------------------------------------------------------ single instructions
+// OP 0: v_exp_f32; 1: v_fma_f32; 2: v_cvt_pk_f16_f32; 3: v_dot2c_f32_f16;
+// 4: 4 MFMA 32x32x16 f16 with 16 independent v_fma_f32 between them.
+// 8 independent dependency chains per wave; each iteration issues 8 of the
+// instruction (OP 4: 4 MFMAs and 16 FMAs).  Registers only.
+template <int OP>
+__global__ void op_rate(float *out, int iters, long long *cycles)
+{
+    float x[8];
+    for (int i = 0; i < 8; ++i) x[i] = 1e-3f * (threadIdx.x + i);
+    f16x8 a;
+    for (int i = 0; i < 8; ++i) a[i] = (_Float16)(1e-3f * i);
+    f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    const f16x2 one = {1, 1};
+    const long long t0 = clock64();
+    for (int it = 0; it < iters; ++it) {
+        if (OP == 4) {
+            c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, a, c0, 0, 0, 0);
+            for (int i = 0; i < 4; ++i) x[i] = fmaf(x[i], 0.999f, 1e-3f);
+            c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, a, c1, 0, 0, 0);
+            for (int i = 4; i < 8; ++i) x[i] = fmaf(x[i], 0.999f, 1e-3f);
+            c2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, a, c2, 0, 0, 0);
+            for (int i = 0; i < 4; ++i) x[i] = fmaf(x[i], 0.999f, 1e-3f);
+            c3 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, a, c3, 0, 0, 0);
+            for (int i = 4; i < 8; ++i) x[i] = fmaf(x[i], 0.999f, 1e-3f);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (OP == 0) x[i] = __builtin_amdgcn_exp2f(-x[i]);
+                if (OP == 1) x[i] = fmaf(x[i], 0.999f, 1e-3f);
+                if (OP == 2) {
+                    const f16x2 h = __builtin_convertvector((float __attribute__((ext_vector_type(2)))){x[i], x[(i + 1) % 8]}, f16x2);
+                    x[i] = __builtin_bit_cast(float, h);
+                }
+                if (OP == 3) x[i] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x[(i + 1) % 8]), one, x[i], false);
+            }
+        }
+    }
+    const long long t1 = clock64();
+    float r = 0.f;
+    for (int i = 0; i < 8; ++i) r += x[i];
+    for (int i = 0; i < 16; ++i) r += c0[i] + c1[i] + c2[i] + c3[i];
+    out[blockIdx.x * blockDim.x + threadIdx.x] = r;
+    if (threadIdx.x % 64 == 0) cycles[blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64] = t1 - t0;
+}
+
+template <int OP>
+static int time_op(const char *name, int waves_per_simd, int cus, float *out, long long *cyc)
+{
+    const int threads = 256 * waves_per_simd, iters = 2000;
+    hipLaunchKernelGGL(op_rate<OP>, dim3(cus), dim3(threads), 0, 0, out, iters, cyc);
+    CHECK_HIP(hipDeviceSynchronize());
+    hipLaunchKernelGGL(op_rate<OP>, dim3(cus), dim3(threads), 0, 0, out, iters, cyc);
+    CHECK_HIP(hipDeviceSynchronize());
+    // the slowest wave's cycles: with several waves per SIMD the oldest one
+    // runs ahead, and only the last one to finish shows what the SIMD does
+    const int n = cus * threads / 64;
+    std::vector<long long> c(n);
+    CHECK_HIP(hipMemcpy(c.data(), cyc, sizeof(long long) * n, hipMemcpyDeviceToHost));
+    long long slowest = 0;
+    for (long long v : c) slowest = v > slowest ? v : slowest;
+    const double per_wave = (double)slowest / iters / (OP == 4 ? 1 : 8);
+    std::printf("%-44s waves/SIMD %d  %7.2f clocks per %s per wave (slowest wave), %6.2f per SIMD\n", name,
+                waves_per_simd, per_wave, OP == 4 ? "iteration" : "instruction", per_wave / waves_per_simd);
+    return 0;
+}
+
 static int run_rates()
 {
     hipDeviceProp_t prop;
@@ -234,7 +307,7 @@ static int run_rates()
     float *out;
     long long *cyc;
     CHECK_HIP(hipMalloc(&out, (size_t)cus * 1024 * sizeof(float)));
-    CHECK_HIP(hipMalloc(&cyc, sizeof(long long)));
+    CHECK_HIP(hipMalloc(&cyc, (size_t)cus * 16 * sizeof(long long)));  // one per wave, up to 16 per CU
     int rc = 0;
     rc |= time_mode<0>("16 MFMA 32x32x16 f16", 1, cus, out, cyc);
     rc |= time_mode<1>("softmax VALU mix of one 64-key tile", 1, cus, out, cyc);
@@ -242,18 +315,93 @@ static int run_rates()
     rc |= time_mode<2>("both in every wave", 1, cus, out, cyc);
     rc |= time_mode<2>("both in every wave", 2, cus, out, cyc);
     rc |= time_mode<3>("MFMA-only wave beside VALU-only wave", 2, cus, out, cyc);
+    for (int w : {1, 4}) {
+        rc |= time_op<0>("v_exp_f32", w, cus, out, cyc);
+        rc |= time_op<1>("v_fma_f32", w, cus, out, cyc);
+        rc |= time_op<2>("v_cvt_pk_f16_f32", w, cus, out, cyc);
+        rc |= time_op<3>("v_dot2c_f32_f16", w, cus, out, cyc);
+    }
+    rc |= time_op<4>("4 MFMA (128 clocks) + 16 independent fma", 1, cus, out, cyc);
     CHECK_HIP(hipFree(out));
     CHECK_HIP(hipFree(cyc));
     return rc;
 }
 
+// ------------------------------------------------------------------ HBM read rate
+// Wave w reads 4 KiB blocks order[w*per .. w*per+per-1] (entries past nblk
+// are skipped), 16 bytes per lane per load; one word per lane is written.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void read_blocks(const u32x4 *x, const int *order, int per, int nblk, unsigned *out)
+{
+    const int w = blockIdx.x * 4 + threadIdx.x / 64, lane = threadIdx.x % 64;
+    unsigned acc = 0;
+    for (int i = 0; i < per; ++i) {
+        const int bi = w * per + i;
+        if (bi >= nblk) break;
+        const int64_t blk = order[bi];
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = x[blk * 256 + u * 64 + lane];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].w;
+    }
+    out[w * 64 + lane] = acc;
+}
+
+static int run_read()
+{
+    const int nblk = 810652;  // 3.32 GB
+    const int waves = 4096;
+    const int per = (nblk + waves - 1) / waves;
+    u32x4 *x;
+    unsigned *out;
+    int *order;
+    CHECK_HIP(hipMalloc(&x, (size_t)nblk * 4096));
+    CHECK_HIP(hipMalloc(&out, sizeof(unsigned) * 64 * waves));
+    CHECK_HIP(hipMalloc(&order, sizeof(int) * nblk));
+    CHECK_HIP(hipMemset(x, 1, (size_t)nblk * 4096));
+    std::vector<int> h(nblk);
+    for (int pass = 0; pass < 2; ++pass) {
+        for (int i = 0; i < nblk; ++i) h[i] = i;
+        if (pass == 1) {  // seeded Fisher-Yates shuffle (64-bit LCG)
+            unsigned long long st = 12345;
+            for (int i = nblk - 1; i > 0; --i) {
+                st = st * 6364136223846793005ULL + 1442695040888963407ULL;
+                const int j = (int)((st >> 33) % (unsigned long long)(i + 1));
+                const int t = h[i];
+                h[i] = h[j];
+                h[j] = t;
+            }
+        }
+        CHECK_HIP(hipMemcpy(order, h.data(), sizeof(int) * nblk, hipMemcpyHostToDevice));
+        hipLaunchKernelGGL(read_blocks, dim3(waves / 4), dim3(256), 0, 0, x, order, per, nblk, out);
+        CHECK_HIP(hipDeviceSynchronize());
+        hipEvent_t e0, e1;
+        CHECK_HIP(hipEventCreate(&e0));
+        CHECK_HIP(hipEventCreate(&e1));
+        CHECK_HIP(hipEventRecord(e0));
+        for (int r = 0; r < 10; ++r)
+            hipLaunchKernelGGL(read_blocks, dim3(waves / 4), dim3(256), 0, 0, x, order, per, nblk, out);
+        CHECK_HIP(hipEventRecord(e1));
+        CHECK_HIP(hipEventSynchronize(e1));
+        float ms = 0;
+        CHECK_HIP(hipEventElapsedTime(&ms, e0, e1));
+        ms /= 10;
+        std::printf("read %.2f GB as 4 KiB blocks, %-6s order: %.3f ms  %.0f GB/s\n", nblk * 4096e-9,
+                    pass ? "random" : "linear", ms, nblk * 4096.0 / (ms * 1e-3) / 1e9);
+    }
+    CHECK_HIP(hipFree(x));
+    CHECK_HIP(hipFree(out));
+    CHECK_HIP(hipFree(order));
+    return 0;
+}
+
 int main(int argc, char **argv)
 {
-    const bool check = argc > 1 && std::strcmp(argv[1], "--check") == 0;
-    const bool rates_ = argc > 1 && std::strcmp(argv[1], "--rates") == 0;
-    if (!check && !rates_) {
-        std::printf("usage: %s --check | --rates\n", argv[0]);
-        return 2;
-    }
-    return check ? run_checks() : run_rates();
+    const char *mode = argc > 1 ? argv[1] : "";
+    if (std::strcmp(mode, "--check") == 0) return run_checks();
+    if (std::strcmp(mode, "--rates") == 0) return run_rates();
+    if (std::strcmp(mode, "--read") == 0) return run_read();
+    std::printf("usage: %s --check | --rates | --read\n", argv[0]);
+    return 2;
 }

@@ -96,6 +96,24 @@ def workload_inputs(w: Workload):
     return make_qkv(w.B, w.H, w.H_kv, w.L, w.d, w.dtype, w.seed)
 
 
+def randn_device(shape, dtype: str, gen: torch.Generator):
+    """A tensor of iid N(0,1) rounded to `dtype`, drawn on gen's device one
+    index of the first dimension at a time (bounding the fp32 temporary): for
+    tensors too large to draw on the host."""
+    t = torch.empty(shape, dtype=TORCH_DTYPES[dtype], device=gen.device)
+    for i in range(shape[0]):
+        t[i] = torch.randn(tuple(shape[1:]), generator=gen, device=gen.device, dtype=torch.float32).to(t.dtype)
+    return t
+
+
+def make_qkv_device(B: int, H: int, H_kv: int, L: int, d: int, dtype: str, seed: int, device):
+    """As make_qkv, drawn on `device` by its own seeded generator (so the
+    values differ from make_qkv's for the same seed)."""
+    gen = torch.Generator(device=device).manual_seed(int(seed))
+    return (randn_device((B, H, L, d), dtype, gen), randn_device((B, H_kv, L, d), dtype, gen),
+            randn_device((B, H_kv, L, d), dtype, gen))
+
+
 def sample_rows(B: int, H: int, L: int, n_random: int, seed: int, tile: int = 64):
     """Flat row ids (b*H + h)*L + i to check at sizes the oracle cannot do whole.
 

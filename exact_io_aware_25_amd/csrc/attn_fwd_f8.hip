@@ -65,10 +65,13 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const void *generic_lds_ptr)
     return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2 *)p);
 }
 
-// four fp32 values -> four E4M3 bytes of one dword (round to nearest even)
+// four fp32 values -> four E4M3 bytes of one dword (round to nearest even).
+// Each conversion writes one half of the dword and keeps the other; the
+// first keeps half of a's own bits, which the second then overwrites, so the
+// result can take a's register (with 0 there it needs a zeroed register).
 __device__ __forceinline__ int pack4_f8(float a, float b, float c, float d)
 {
-    int x = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    int x = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false);
     return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, x, true);
 }
 
@@ -249,13 +252,13 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_f8_kernel(F8Params p)
         f32x16 w[2];
         float l_tile = 0.f;
         auto weights = [&]() {
-            float part[4] = {0.f, 0.f, 0.f, 0.f};
+            float part[4];  // four interleaved fp32 sums, each started from a weight
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     w[kb][r] = __builtin_amdgcn_exp2f(fmaf(s[kb][r], p.scale_log2, neg_m));
-                    part[r % 4] += w[kb][r];
+                    part[r % 4] = (kb == 0 && r < 4) ? w[0][r] : part[r % 4] + w[kb][r];
                 }
             l_tile = (part[0] + part[1]) + (part[2] + part[3]);
         };

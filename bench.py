@@ -393,7 +393,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the library and this benchmark run on one GPU; --gpus {args.gpus} is not supported "
               "(the kernel shards over (batch, head) with no exchange, so N GPUs run N independent "
               "copies).", file=sys.stderr)
         sys.exit(2)

@@ -276,6 +276,10 @@ __global__ __launch_bounds__(64 * NW * SPLIT) void attn_fwd_kernel(Params p)
                         // sum over the tile, started from its first weight
 #pragma unroll
                         for (int e = 0; e < 8; ++e) l_tile = (ks == 0 && e == 0) ? pf[0] : l_tile + pf[e];
+                        // pack here: left to itself the compiler moves the packs past
+                        // the sum check, keeping all 32 fp32 weights live across it
+                        // (11 more VGPRs, one wave per SIMD fewer at d=64)
+                        asm volatile("" : "+v"(pv[ks]));
                     }
                 }
                 // fp16: four independent dot2 chains, combined pairwise (one chain

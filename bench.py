@@ -137,6 +137,51 @@ def time_workload(w, steps: int, warmup: int):
                 peak_mem=peak, peak_mem_incl_inputs=peak, peak_mem_call=peak - base)
 
 
+def data_sensitivity(w, inputs, steps: int):
+    """The same kernel on the same shape with inputs whose values carry fewer
+    significant bits: the seeded N(0,1) inputs, those values rounded to 8
+    significant bits (held in the input type), signed powers of two, and
+    zeros.  The instruction stream is the same in every case (the sum-checked
+    softmax takes its slow path only on each row block's first tile either
+    way), so a change of time is a change of clock: the MFMA arrays draw less
+    power on operands with fewer bits set.  One JSON line per case, to stderr."""
+    q, k, v = inputs
+    dt = q.dtype
+
+    def fewer_bits(t):  # bf16 and fp8 values have 8 or fewer significant bits already
+        return t.to(torch.bfloat16).to(dt) if dt == torch.float16 else t
+
+    def pow2(t):
+        f = t.float()
+        return (torch.sign(f) * torch.exp2(torch.round(torch.log2(f.abs().clamp(min=2.0 ** -14))))).to(dt)
+
+    cases = [("seeded N(0,1)", (q, k, v)), ("8 significant bits", tuple(fewer_bits(t) for t in (q, k, v))),
+             ("signed powers of two", tuple(pow2(t) for t in (q, k, v))),
+             ("zeros", tuple(torch.zeros_like(t) for t in (q, k, v)))]
+    stream = torch.cuda.current_stream()
+    out = torch.empty(q.shape, dtype=torch.bfloat16 if w.dtype == "f8" else dt, device=q.device)
+    lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=q.device)
+    # two passes over the cases, so that a drift of the clock over the run
+    # (it differs from the first case to the last) shows as a difference
+    # between the passes rather than between the cases
+    for pass_no, (name, (a, b, c)) in [(p, nc) for p in (1, 2) for nc in cases]:
+        for _ in range(3):
+            attn.forward(a, b, c, causal=w.causal, window=w.window, scale=w.scale, out=out, lse=lse, stream=stream)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            attn.forward(a, b, c, causal=w.causal, window=w.window, scale=w.scale, out=out, lse=lse, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        tf = algorithmic_flops(w) / (ms * 1e-3) / 1e12
+        print(json.dumps({"data_sensitivity": name, "pass": pass_no, "workload": w.name, "ms": round(ms, 4),
+                          "tflops": round(tf, 1), "pct_of_mfma_peak": round(100 * tf / mfma_peak(w), 2)}),
+              file=sys.stderr, flush=True)
+
+
 def decode_bytes(w) -> float:
     """Algorithmic bytes of one decode step: every K/V row some query row
     sees, once per K/V head, plus q and out (16-bit), lse (fp32), the page
@@ -379,6 +424,9 @@ def main():
     ap.add_argument("--workload", default=None, choices=sorted(WORKLOADS) + sorted(DECODE_WORKLOADS))
     ap.add_argument("--sweep", action="store_true",
                     help="also time every workload and print one extra JSON line each (to stderr)")
+    ap.add_argument("--data-sensitivity", action="store_true",
+                    help="also time the workload's kernel on inputs with fewer significant bits (same "
+                         "shape, same instructions) and print one extra JSON line each (to stderr)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode", action="store_true",
@@ -443,6 +491,9 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, r["out"], r["lse"], r["inputs"], args.cpu_budget)
     print(json.dumps(line), flush=True)
+
+    if args.data_sensitivity:
+        data_sensitivity(w, r["inputs"], max(5, args.steps))
 
     if args.sweep:
         del r, line

@@ -21,6 +21,7 @@
 // Every memory access stays inside the buffers it is given.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <vector>
@@ -230,6 +231,76 @@ static int time_mode(const char *name, int waves_per_simd, int cus, float *out, 
     return 0;
 }
 
+// ------------------------------------------------------------------ MFMA on random operands
+// 16 MFMA 32x32x16 f16 per iteration (4 accumulators), the A and B operands
+// taken in turn from 8 fragments per lane of N(0,1) fp16 values (read once
+// from `src`, 64 lanes x 8 fragments x 8 halves per wave), so the operand
+// bits change from one instruction to the next as they do in the attention
+// kernel.  MFMA power, and so the clock, depends on those bits.
+__global__ void mfma_random(const f16x8 *src, float *out, int iters, long long *cycles)
+{
+    const int lane = threadIdx.x % 64;
+    f16x8 frag[8];
+    for (int i = 0; i < 8; ++i) frag[i] = src[(threadIdx.x / 64 % 4) * 512 + i * 64 + lane];
+    f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    const long long t0 = clock64();
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(frag[2 * i], frag[2 * i + 1], c0, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(frag[(2 * i + 2) % 8], frag[(2 * i + 5) % 8], c1, 0, 0, 0);
+            c2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(frag[(2 * i + 4) % 8], frag[(2 * i + 1) % 8], c2, 0, 0, 0);
+            c3 = __builtin_amdgcn_mfma_f32_32x32x16_f16(frag[(2 * i + 6) % 8], frag[(2 * i + 7) % 8], c3, 0, 0, 0);
+        }
+    }
+    const long long t1 = clock64();
+    float r = 0.f;
+    for (int i = 0; i < 16; ++i) r += c0[i] + c1[i] + c2[i] + c3[i];
+    out[blockIdx.x * blockDim.x + threadIdx.x] = r;
+    if (threadIdx.x == 0 && blockIdx.x == 0) cycles[0] = t1 - t0;
+}
+
+static int time_mfma_random(int waves_per_simd, int cus, float *out, long long *cyc)
+{
+    // 4 waves' worth of fragments (2048 x 8 halves), N(0,1) by Box-Muller on a
+    // seeded 64-bit LCG, rounded to fp16; waves w and w+4 share a set
+    std::vector<_Float16> h(4 * 512 * 8);
+    unsigned long long st = 2024;
+    auto uni = [&]() {
+        st = st * 6364136223846793005ULL + 1442695040888963407ULL;
+        return ((st >> 11) + 0.5) * (1.0 / 9007199254740992.0);
+    };
+    for (size_t i = 0; i < h.size(); i += 2) {
+        const double r = std::sqrt(-2.0 * std::log(uni())), t = 6.283185307179586 * uni();
+        h[i] = (_Float16)(r * std::cos(t));
+        h[i + 1] = (_Float16)(r * std::sin(t));
+    }
+    f16x8 *src;
+    CHECK_HIP(hipMalloc(&src, h.size() * sizeof(_Float16)));
+    CHECK_HIP(hipMemcpy(src, h.data(), h.size() * sizeof(_Float16), hipMemcpyHostToDevice));
+    const int threads = 256 * waves_per_simd, iters = 1000;
+    hipLaunchKernelGGL(mfma_random, dim3(cus), dim3(threads), 0, 0, src, out, iters, cyc);
+    CHECK_HIP(hipDeviceSynchronize());
+    hipEvent_t e0, e1;
+    CHECK_HIP(hipEventCreate(&e0));
+    CHECK_HIP(hipEventCreate(&e1));
+    CHECK_HIP(hipEventRecord(e0));
+    for (int r = 0; r < 20; ++r)
+        hipLaunchKernelGGL(mfma_random, dim3(cus), dim3(threads), 0, 0, src, out, iters, cyc);
+    CHECK_HIP(hipEventRecord(e1));
+    CHECK_HIP(hipEventSynchronize(e1));
+    float ms = 0;
+    CHECK_HIP(hipEventElapsedTime(&ms, e0, e1));
+    ms /= 20;
+    const double tflops = threads / 64.0 * 16 * 32768.0 * iters * cus / (ms * 1e-3) / 1e12;
+    std::printf("%-44s waves/SIMD %d  %8.3f ms  MFMA %7.1f TFLOP/s\n", "16 MFMA 32x32x16 f16, N(0,1) operands",
+                waves_per_simd, ms, tflops);
+    CHECK_HIP(hipFree(src));
+    CHECK_HIP(hipEventDestroy(e0));
+    CHECK_HIP(hipEventDestroy(e1));
+    return 0;
+}
+
 // ------------------------------------------------------------------ single instructions
 // OP 0: v_exp_f32; 1: v_fma_f32; 2: v_cvt_pk_f16_f32; 3: v_dot2c_f32_f16;
 // 4: 4 MFMA 32x32x16 f16 with 16 independent v_fma_f32 between them.
@@ -315,6 +386,8 @@ static int run_rates()
     rc |= time_mode<2>("both in every wave", 1, cus, out, cyc);
     rc |= time_mode<2>("both in every wave", 2, cus, out, cyc);
     rc |= time_mode<3>("MFMA-only wave beside VALU-only wave", 2, cus, out, cyc);
+    rc |= time_mfma_random(1, cus, out, cyc);
+    rc |= time_mfma_random(2, cus, out, cyc);
     for (int w : {1, 4}) {
         rc |= time_op<0>("v_exp_f32", w, cus, out, cyc);
         rc |= time_op<1>("v_fma_f32", w, cus, out, cyc);

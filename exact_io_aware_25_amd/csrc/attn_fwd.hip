@@ -231,12 +231,12 @@ __global__ __launch_bounds__(64 * NW * SPLIT) void attn_fwd_kernel(Params p)
                     for (int ds = 0; ds < kDSteps; ++ds)
                         kf[kb][ds] = *reinterpret_cast<const vec8 *>(tk + 32 * kb * kRowBytes + koff[ds]);
                 __builtin_amdgcn_sched_barrier(0);
+                s[0] = f32x16{};
+                s[1] = f32x16{};
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    s[kb] = f32x16{};
+                for (int ds = 0; ds < kDSteps; ++ds)
 #pragma unroll
-                    for (int ds = 0; ds < kDSteps; ++ds) s[kb] = mfma32(kf[kb][ds], qf[ds], s[kb]);
-                }
+                    for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32(kf[kb][ds], qf[ds], s[kb]);
             }
 
             __builtin_amdgcn_s_setprio(0);

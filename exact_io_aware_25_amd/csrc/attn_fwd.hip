@@ -412,14 +412,17 @@ hipError_t launch_waves(Params p, hipStream_t stream)
                            grid, dim3(64 * NW * SPLIT), kargs, 0, stream);
 }
 
-// Workgroup shape: waves per key-range group (4 -> 128 query rows, 8 -> 256)
-// and number of key-range groups.  Measured on MI355X: 8-wave groups halve
-// K/V traffic per FLOP and win once the 256-row grid has >= 512 blocks; plain
-// causal grids have unequal blocks (the last one walks every key), so below
-// 2048 blocks their serial key loop is split (2 groups of 8 waves at d=64,
-// else 4 groups of 4 waves); other small grids split in 2.  Limits: a
-// 16-wave workgroup must fit 128 VGPRs per wave, which d=128 does not, and
-// four d=128 splits would not fit LDS.
+// Workgroup shape: waves per key-range group (2 -> 64 query rows, 4 -> 128,
+// 8 -> 256) and number of key-range groups.  Measured on MI355X: 8-wave
+// groups halve K/V traffic per FLOP and win once the 256-row grid has >= 512
+// blocks; plain causal grids have unequal blocks (the last one walks every
+// key), so below 2048 blocks their serial key loop is split (2 groups of 8
+// waves at d=64, else 4 groups of 4 waves).  The shortest plain causal grids
+// (<= 256 blocks of 128 rows: 4k and 8k tokens at 4 heads) are held by the
+// last block's walk on one CU; at d=64, 64-row workgroups of 4 groups of 2
+// waves halve it (causal 4k, H=4: 38 -> 28 us; 8k: 70 -> 62 us).  Other small
+// grids split in 2.  Limits: a 16-wave workgroup must fit 128 VGPRs per
+// wave, which d=128 does not, and four d=128 splits would not fit LDS.
 void launch_shape(int64_t B, int64_t H, int64_t L, int d, bool causal, int window, int *waves, int *splits)
 {
     const int64_t g8 = (L + 255) / 256 * B * H;
@@ -433,8 +436,12 @@ void launch_shape(int64_t B, int64_t H, int64_t L, int d, bool causal, int windo
         return;
     }
     *waves = 4;
-    if (unequal) *splits = d == 64 ? 4 : 2;
-    else *splits = g4 < 512 ? 2 : 1;
+    if (unequal) {
+        *splits = d == 64 ? 4 : 2;
+        if (d == 64 && g4 <= 256) *waves = 2;
+    } else {
+        *splits = g4 < 512 ? 2 : 1;
+    }
 }
 
 template <typename T, int D, bool CAUSAL, bool WINDOW>
@@ -447,6 +454,9 @@ hipError_t launch_instance(const Params &p, hipStream_t stream)
             if (splits == 2) return launch_waves<T, D, CAUSAL, WINDOW, 8, 2>(p, stream);
         }
         return launch_waves<T, D, CAUSAL, WINDOW, 8, 1>(p, stream);
+    }
+    if constexpr (D == 64 && CAUSAL && !WINDOW) {
+        if (waves == 2) return launch_waves<T, D, CAUSAL, WINDOW, 2, 4>(p, stream);
     }
     if constexpr (D == 64) {
         if (splits == 4) return launch_waves<T, D, CAUSAL, WINDOW, 4, 4>(p, stream);

@@ -101,7 +101,9 @@ def test_launch_shape():
     assert shape(1, 4, 131072, 64, True, -1) == (8, 1)      # long causal: 2048 blocks of 256 rows
     assert shape(1, 4, 32768, 64, True, -1) == (8, 2)       # mid causal: split the key loop in 2
     assert shape(1, 4, 32768, 128, True, -1) == (8, 1)      # d=128 cannot run 16-wave groups
-    assert shape(1, 4, 4096, 64, True, -1) == (4, 4)        # short causal: 4 key splits
+    assert shape(1, 4, 4096, 64, True, -1) == (2, 4)        # short causal: 64-row blocks, 4 key splits
+    assert shape(1, 4, 8192, 64, True, -1) == (2, 4)
+    assert shape(1, 4, 16384, 64, True, -1) == (4, 4)       # 512 blocks of 128 rows: 4-wave groups
     assert shape(1, 4, 4096, 128, True, -1) == (4, 2)
     assert shape(2, 8, 2048, 64, False, -1) == (4, 2)       # short non-causal
     assert shape(1, 32, 16384, 128, True, 4096) == (8, 1)   # windowed: blocks of equal work
@@ -111,8 +113,9 @@ def test_launch_shape():
             for window in (-1, 0, 100):
                 for B, H, L in ((1, 1, 1), (2, 8, 300), (1, 64, 65536), (3, 5, 777)):
                     waves, splits = shape(B, H, L, d, causal, window)
-                    assert waves in (4, 8) and splits in (1, 2, 4)
+                    assert waves in (2, 4, 8) and splits in (1, 2, 4)
                     assert not (d == 128 and splits == 4) and not (waves == 8 and splits == 4)
+                    assert waves != 2 or (d == 64 and causal and window < 0 and splits == 4)
                     assert not (waves == 8 and splits == 2 and d == 128)
     with pytest.raises(ValueError):
         shape(1, 4, 100, 96, True, -1)

@@ -265,14 +265,17 @@ def test_errors_raise_before_launch():
 
 
 # ------------------------------------------------------------------ every launch shape
-# The library picks, per problem, 4- or 8-wave key-range groups (128 or 256
-# query rows per workgroup) and 1, 2 or 4 key-range groups merged at the end.
+# The library picks, per problem, 2-, 4- or 8-wave key-range groups (64, 128
+# or 256 query rows per workgroup) and 1, 2 or 4 key-range groups merged at
+# the end.
 # Each case below is a shape that attn_launch_shape confirms takes a given
 # path; sampled rows (first and last of heads, tile, block and split
 # boundaries, the ragged tail) are checked against the oracle.
 SHAPE_CASES = [
     # (waves, splits, d, dtype, causal, window, B, H, H_kv, L)
-    (4, 4, 64, "f16", True, -1, 1, 4, 2, 300),
+    (2, 4, 64, "f16", True, -1, 1, 4, 2, 300),
+    (2, 4, 64, "bf16", True, -1, 2, 3, 1, 777),
+    (4, 4, 64, "f16", True, -1, 1, 8, 2, 4500),
     (4, 2, 128, "bf16", True, -1, 1, 4, 1, 300),
     (4, 2, 64, "bf16", False, -1, 2, 4, 4, 333),
     (4, 2, 128, "f16", True, 37, 1, 8, 2, 300),

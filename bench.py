@@ -426,7 +426,8 @@ def main():
                     help="also time every workload and print one extra JSON line each (to stderr)")
     ap.add_argument("--data-sensitivity", action="store_true",
                     help="also time the workload's kernel on inputs with fewer significant bits (same "
-                         "shape, same instructions) and print one extra JSON line each (to stderr)")
+                         "shape, same instructions) and print one extra JSON line each (to stderr); "
+                         "with --backward: N(0,1) and zero inputs")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode", action="store_true",
@@ -695,6 +696,41 @@ def main_backward(w, args):
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_bwd(w, r["dq"], r["inputs"], args.cpu_budget)
     print(json.dumps(line), flush=True)
+    if args.data_sensitivity:
+        data_sensitivity_bwd(w, r["inputs"], max(3, args.steps // 4))
+
+
+def data_sensitivity_bwd(w, inputs, steps: int):
+    """The backward pass on the seeded N(0,1) inputs and on zeros (same
+    instruction stream), two passes; one JSON line per case, to stderr.  As for
+    the forward, a change of time is a change of clock."""
+    q, k, v, g = inputs
+    stream = torch.cuda.current_stream()
+    ws = torch.empty(attn.attn_bwd_workspace_size(w.B, w.H, w.L), dtype=torch.uint8, device=q.device)
+    cases = [("seeded N(0,1)", (q, k, v, g)), ("zeros", tuple(torch.zeros_like(t) for t in (q, k, v, g)))]
+    for pass_no, (name, (a, b, c, d)) in [(p, nc) for p in (1, 2) for nc in cases]:
+        out, lse = attn.forward(a, b, c, causal=w.causal, window=w.window, scale=w.scale, stream=stream)
+        dq, dk, dv = torch.empty_like(a), torch.empty_like(b), torch.empty_like(c)
+
+        def step():
+            attn.backward(a, b, c, out, lse, d, causal=w.causal, window=w.window, scale=w.scale,
+                          dq=dq, dk=dk, dv=dv, workspace=ws, stream=stream)
+        for _ in range(2):
+            step()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        tf = algorithmic_flops_bwd(w) / (ms * 1e-3) / 1e12
+        print(json.dumps({"data_sensitivity": name, "pass": pass_no, "workload": w.name, "backward": True,
+                          "ms": round(ms, 4), "tflops": round(tf, 1),
+                          "pct_of_mfma_peak": round(100 * tf / MFMA_PEAK_F16_TFLOPS, 2)}),
+              file=sys.stderr, flush=True)
 
 
 if __name__ == "__main__":

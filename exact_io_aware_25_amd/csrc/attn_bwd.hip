@@ -330,6 +330,245 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 12 / NW : 1) void attn_bwd_dkdv_
         }
 }
 
+// ---------------------------------------------------------------- 2b. dK, dV with wave pairs (d=128)
+// At d=128 one wave's dK^T and dV^T accumulators (128 VGPRs) plus its K and
+// V fragments leave room for one wave per SIMD.  Here the two halves of the
+// work go to a pair of waves that own the same 32 keys: wave A holds K and
+// accumulates dV (S = Q K^T, P, dV^T += dO^T P), wave B holds V and
+// accumulates dK (dP = dO V^T, dS = P (dP - D), dK^T += Q^T dS).  A hands
+// each 32-query block's P (fp32, in its own register order) to B through a
+// double-buffered LDS slot, behind one barrier per block.  A workgroup holds
+// NP pairs (32*NP keys): waves 0..NP-1 are the A waves, NP..2NP-1 the B
+// waves, so each SIMD hosts one of each.
+template <typename T, int D, bool CAUSAL, bool WINDOW, int NP>
+__global__ __launch_bounds__(128 * NP) void attn_bwd_dkdv_pair_kernel(BwdParams p)
+{
+    typedef typename Vec8<T>::type vec8;
+    constexpr int NW = 2 * NP;                           // waves per workgroup
+    constexpr int kThreads = 64 * NW;
+    constexpr int kBlockKV = kRowsPerWave * NP;          // keys per workgroup
+    constexpr int kRowBytes = 2 * D;
+    constexpr int kTileBytes = kTileQ * kRowBytes;       // one Q or dO tile
+    constexpr int kWsBytes = 1024;                       // -lse*log2e and -D of 64 rows, + zero fill
+    constexpr int kStageBytes = 2 * kTileBytes + kWsBytes;
+    constexpr int kUnits = D / 8;
+    constexpr int kChunks = kTileQ * kUnits / kThreads;  // 16-byte units per thread per tile
+    constexpr int kDSteps = D / 16;
+    constexpr int kDBlocks = D / 32;
+    static_assert(kChunks * kThreads == kTileQ * kUnits, "tile copy must split evenly");
+
+    __shared__ __attribute__((aligned(16))) char lds_a[kStageBytes];
+    __shared__ __attribute__((aligned(16))) char lds_b[kStageBytes];
+    __shared__ __attribute__((aligned(16))) float xbuf[2][NP][16 * 64];  // P of a 32-query block, per pair
+
+    const int tid = threadIdx.x;
+    const int wave = tid / 64;
+    const int lane = tid % 64;
+    const int l32 = lane % 32;
+    const int hi = lane / 32;
+    const int role = __builtin_amdgcn_readfirstlane(wave / NP);  // 0: S, P, dV   1: dP, dS, dK
+    const int pair = wave % NP;
+
+    const int BG = p.B * p.H_kv;
+    const int kblk = blockIdx.x / BG;
+    const int bg = blockIdx.x % BG;
+    const int b = bg / p.H_kv;
+    const int g = bg % p.H_kv;
+    const int L = p.L;
+    const int k_first = kblk * kBlockKV;
+    const int k_last = min(L, k_first + kBlockKV) - 1;
+
+    int q_begin = 0, q_end = L;
+    if (CAUSAL) q_begin = k_first;
+    else if (WINDOW) q_begin = max(0, k_first - p.window);
+    if (WINDOW) q_end = min(L, k_last + p.window + 1);
+    const int tq_first = q_begin / kTileQ;
+    const int n_tq = (q_end + kTileQ - 1) / kTileQ - tq_first;
+    const int n_steps = p.group * n_tq;
+
+    // ---- this pair's keys; wave A keeps K fragments, wave B V fragments
+    const int ka = k_first + pair * kRowsPerWave;
+    const int kz = min(ka + kRowsPerWave, L) - 1;
+    const bool pair_live = ka < L;
+    const int kj = ka + l32;
+    const T *kvh = static_cast<const T *>(role == 0 ? p.k : p.v) + ((int64_t)b * p.H_kv + g) * L * D;
+    vec8 bfrag[kDSteps];
+#pragma unroll
+    for (int s = 0; s < kDSteps; ++s)
+        bfrag[s] = kj < L ? *reinterpret_cast<const vec8 *>(kvh + (int64_t)kj * D + 16 * s + 8 * hi) : vec8{};
+    f32x16 acc[kDBlocks];  // A: dV^T, B: dK^T
+#pragma unroll
+    for (int i = 0; i < kDBlocks; ++i) acc[i] = f32x16{};
+
+    // ---- per-lane LDS byte offsets (as in the single-wave kernel)
+    const int qrow = k_row_for_lane(l32);
+    int roff[kDSteps];
+#pragma unroll
+    for (int ds = 0; ds < kDSteps; ++ds)
+        roff[ds] = qrow * kRowBytes + 16 * ((2 * ds + hi) ^ dual_swizzle<D>(qrow));
+    const int tr_row = 8 * hi + ((lane >> 2) & 3);
+    const int tr_unit = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    int troff[kDBlocks][2];
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 2; ++r4) {
+            const int row = tr_row + 4 * r4;
+            troff[db][r4] = row * kRowBytes + 16 * ((4 * db + tr_unit) ^ dual_swizzle<D>(row)) + 8 * (lane & 1);
+        }
+    int ld_off[kChunks];
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+        const int unit_idx = (c * NW + wave) * 64 + lane;
+        const int row = unit_idx / kUnits, phys = unit_idx % kUnits;
+        ld_off[c] = row * kRowBytes + 16 * (phys ^ dual_swizzle<D>(row));
+    }
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+
+    auto copy_step = [&](int n, char *stage) {
+        const int hh = n / n_tq;
+        const int q0 = (tq_first + n % n_tq) * kTileQ;
+        const int64_t bh = (int64_t)b * p.H + g * p.group + hh;
+        const int bytes = min(L - q0, kTileQ) * kRowBytes;
+        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(static_cast<const T *>(p.q) + (bh * L + q0) * D), 0, bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(static_cast<const T *>(p.dout) + (bh * L + q0) * D), 0, bytes, 0x00020000);
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+            const int region = (c * NW + wave_u) * 1024;
+            copy_to_lds16(rq, stage + region, ld_off[c]);
+            copy_to_lds16(rg, stage + kTileBytes + region, ld_off[c]);
+        }
+        if (wave_u == NW - 1) {
+            const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(p.ws + bh * 2 * p.Lp), 0, 2 * p.Lp * 4, 0x00020000);
+            const int off = lane < 16 ? 4 * (q0 + 4 * lane)
+                            : lane < 32 ? 4 * (p.Lp + q0 + 4 * (lane - 16)) : 8 * p.Lp;
+            copy_to_lds16(rw, stage + 2 * kTileBytes, off);
+        }
+    };
+
+    if (n_steps > 0) copy_step(0, lds_a);
+
+    // Every wave meets the same barriers: one per step and one per 32-query
+    // block, whether or not its pair has work in the step.
+    auto process = [&](int n, char *cur, char *nxt) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
+        __syncthreads();
+        if (n + 1 < n_steps) copy_step(n + 1, nxt);
+
+        const int q0 = (tq_first + n % n_tq) * kTileQ;
+        const int q9 = q0 + kTileQ - 1;
+        bool skip = !pair_live;
+        if (CAUSAL) skip = skip || q9 < ka;
+        if (WINDOW) {
+            skip = skip || q0 - kz > p.window;
+            if (!CAUSAL) skip = skip || ka - q9 > p.window;
+        }
+        bool full = q9 < L;
+        if (CAUSAL) full = full && q0 >= kz;
+        if (WINDOW) {
+            full = full && q9 - ka <= p.window;
+            if (!CAUSAL) full = full && kz - q0 <= p.window;
+        }
+        const char *tq = cur;
+        const char *tg = cur + kTileBytes;
+        const float *tw = reinterpret_cast<const float *>(cur + 2 * kTileBytes);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            float *xb = &xbuf[qb][pair][0];
+            vec8 pv[2];
+            f32x16 dp;
+            if (!skip) {
+                if (role == 0) {
+                    // S = Q K^T; register r of lane half hi holds query
+                    // q0 + 32qb + 16(r/8) + 8hi + r%8
+                    f32x16 s = f32x16{};
+                    vec8 af[kDSteps];
+#pragma unroll
+                    for (int ds = 0; ds < kDSteps; ++ds)
+                        af[ds] = *reinterpret_cast<const vec8 *>(tq + 32 * qb * kRowBytes + roff[ds]);
+#pragma unroll
+                    for (int ds = 0; ds < kDSteps; ++ds) s = mfma32(af[ds], bfrag[ds], s);
+                    if (!full) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int i = q0 + 32 * qb + 16 * (r / 8) + 8 * hi + (r % 8);
+                            if (i >= L || !visible<CAUSAL, WINDOW>(i, kj, L, p.window)) s[r] = -INFINITY;
+                        }
+                    }
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        const int base = 32 * qb + 16 * t + 8 * hi;
+                        f32x8 pf;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            pf[e] = __builtin_amdgcn_exp2f(fmaf(s[8 * t + e], p.scale_log2, tw[base + e]));
+                            xb[(8 * t + e) * 64 + lane] = pf[e];
+                        }
+                        pv[t] = __builtin_convertvector(pf, vec8);
+                    }
+                } else {
+                    // dP starts from -D, so the products give dP - D
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) dp[r] = tw[kTileQ + 32 * qb + 16 * (r / 8) + 8 * hi + (r % 8)];
+                    vec8 gf[kDSteps];
+#pragma unroll
+                    for (int ds = 0; ds < kDSteps; ++ds)
+                        gf[ds] = *reinterpret_cast<const vec8 *>(tg + 32 * qb * kRowBytes + roff[ds]);
+#pragma unroll
+                    for (int ds = 0; ds < kDSteps; ++ds) dp = mfma32(gf[ds], bfrag[ds], dp);
+                }
+            }
+            __syncthreads();  // the block's P is in LDS
+            if (!skip) {
+                if (role == 1) {
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        f32x8 df;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) df[e] = xb[(8 * t + e) * 64 + lane] * dp[8 * t + e];
+                        pv[t] = __builtin_convertvector(df, vec8);  // dS
+                    }
+                }
+                // A: dV^T += dO^T P   B: dK^T += Q^T dS, over the two 16-query slices
+                const char *src = role == 0 ? tg : tq;
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int rbase = (32 * qb + 16 * t) * kRowBytes;
+#pragma unroll
+                    for (int db = 0; db < kDBlocks; ++db) {
+                        const s16x4 lo4 = lds_read_tr16(src + rbase + troff[db][0]);
+                        const s16x4 hi4 = lds_read_tr16(src + rbase + troff[db][1]);
+                        const vec8 at = __builtin_bit_cast(vec8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+                        acc[db] = mfma32(at, pv[t], acc[db]);
+                    }
+                }
+            }
+        }
+    };
+
+    for (int n = 0; n < n_steps; n += 2) {
+        process(n, lds_a, lds_b);
+        if (n + 1 < n_steps) process(n + 1, lds_b, lds_a);
+    }
+
+    // ---- epilogue: register 4a+c of block db holds d = 32db + 8a + 4hi + c of key kj
+    if (!pair_live || kj >= L) return;
+    T *row = static_cast<T *>(role == 0 ? p.dv : p.dk) + (((int64_t)b * p.H_kv + g) * L + kj) * D;
+    const float mul = role == 0 ? 1.f : p.scale;
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            T v4[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) v4[c] = (T)(acc[db][4 * a + c] * mul);
+            *reinterpret_cast<uint64_t *>(row + 32 * db + 8 * a + 4 * hi) = *reinterpret_cast<const uint64_t *>(v4);
+        }
+}
+
 // ---------------------------------------------------------------- 3. dQ
 template <typename T, int D, bool CAUSAL, bool WINDOW, int NW>
 __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_kernel(BwdParams p)
@@ -552,9 +791,11 @@ hipError_t launch_bwd_instance(BwdParams p, hipStream_t stream)
     constexpr int kRows = kRowsPerWave * NW;
     void *kargs[] = {&p};
     p.n_blk = (p.L + kRows - 1) / kRows;
-    hipError_t err = hipLaunchKernel(reinterpret_cast<const void *>(&attn_bwd_dkdv_kernel<T, D, CAUSAL, WINDOW, NW>),
-                                     dim3((unsigned)((int64_t)p.n_blk * p.B * p.H_kv)), dim3(64 * NW), kargs, 0,
-                                     stream);
+    // d=128: wave pairs (4 pairs = the same 128 keys per workgroup)
+    const void *dkdv = D == 128 ? reinterpret_cast<const void *>(&attn_bwd_dkdv_pair_kernel<T, D, CAUSAL, WINDOW, NW>)
+                                : reinterpret_cast<const void *>(&attn_bwd_dkdv_kernel<T, D, CAUSAL, WINDOW, NW>);
+    hipError_t err = hipLaunchKernel(dkdv, dim3((unsigned)((int64_t)p.n_blk * p.B * p.H_kv)),
+                                     dim3(D == 128 ? 128 * NW : 64 * NW), kargs, 0, stream);
     if (err != hipSuccess) return err;
     return hipLaunchKernel(reinterpret_cast<const void *>(&attn_bwd_dq_kernel<T, D, CAUSAL, WINDOW, NW>),
                            dim3((unsigned)((int64_t)p.n_blk * p.B * p.H)), dim3(64 * NW), kargs, 0, stream);

@@ -243,8 +243,9 @@ def backward(q, k, v, out, lse, dout, causal: bool = False, window: int = -1, sc
     need = attn_bwd_workspace_size(B, H, L)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    if workspace.numel() * workspace.element_size() < need or workspace.device != q.device:
-        raise ValueError(f"workspace must hold {need} bytes on q's device")
+    if (workspace.numel() * workspace.element_size() < need or workspace.device != q.device
+            or not workspace.is_contiguous()):
+        raise ValueError(f"workspace must be a contiguous tensor of at least {need} bytes on q's device")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     fn = attn_bwd if q.dtype == torch.float16 else attn_bwd_bf16
@@ -286,15 +287,18 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int, window:
         raise ValueError("shape mismatch between q, caches, block_table and seq_lens")
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, H, Lq), dtype=torch.float32, device=q.device) if lse is None else lse
-    if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor like q")
-    if tuple(lse.shape) != (B, H, Lq) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 tensor [B, H, Lq]")
+    if (tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or not out.is_contiguous()
+            or out.device != q.device):
+        raise ValueError("out must be a contiguous tensor like q, on q's device")
+    if (tuple(lse.shape) != (B, H, Lq) or lse.dtype != torch.float32 or not lse.is_contiguous()
+            or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, Lq] on q's device")
     need = attn_decode_workspace_size(B, H, H_kv, Lq, d, max_seq_len)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    if workspace.numel() * workspace.element_size() < need:
-        raise ValueError(f"workspace must hold {need} bytes")
+    if (workspace.numel() * workspace.element_size() < need or workspace.device != q.device
+            or not workspace.is_contiguous()):
+        raise ValueError(f"workspace must be a contiguous tensor of at least {need} bytes on q's device")
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     fn = attn_decode if q.dtype == torch.float16 else attn_decode_bf16

@@ -315,3 +315,14 @@ def test_bwd_side_stream_and_errors():
     small = torch.empty(8, dtype=torch.uint8, device=DEV)
     with pytest.raises(ValueError):
         attn.backward(q, k, v, out, lse, g, workspace=small)
+
+
+def test_bwd_rejects_strided_workspace():
+    """A workspace view with enough elements but not contiguous is refused."""
+    announce("bwd argument checks")
+    q, k, v = (t.to(DEV) for t in make_qkv(1, 2, 2, 100, 64, "f16", 5))
+    out, lse = attn.forward(q, k, v, causal=True)
+    need = attn.attn_bwd_workspace_size(1, 2, 100)
+    strided = torch.empty(2 * need + 32, dtype=torch.uint8, device=DEV)[::2]
+    with pytest.raises(ValueError):
+        attn.backward(q, k, v, out, lse, torch.randn_like(out), causal=True, workspace=strided)

@@ -104,3 +104,22 @@ def test_decode_lengths_clamped_and_short_sequences():
     check(out[1:2, :, 2:], lse[1:2, :, 2:], ref_o, ref_l, "f16", "short sequence")
     ref_o, ref_l = paged.decode_attention(q[2:3], kc, vc, bt[2:3], [300], "f16", -1, 0.125)
     check(out[2:3], lse[2:3], ref_o, ref_l, "f16", "third sequence")
+
+
+def test_decode_rejects_bad_workspace_and_outputs():
+    """A strided or short workspace, and outputs of the wrong shape, are
+    refused before any launch (ValueError), never written past."""
+    B, H, H_kv, Lq, d, bs = 1, 4, 2, 1, 64, 16
+    announce("decode argument checks")
+    q, kc, vc, bt, sl = (t.to(DEV) for t in make_paged(B, H, H_kv, d, "f16", Lq, [100], bs, seed=3))
+    need = attn.attn_decode_workspace_size(B, H, H_kv, Lq, d, 100)
+    strided = torch.empty(2 * need + 32, dtype=torch.uint8, device=DEV)[::2]
+    with pytest.raises(ValueError):
+        attn.decode(q, kc, vc, bt, sl, 100, workspace=strided)
+    with pytest.raises(ValueError):
+        attn.decode(q, kc, vc, bt, sl, 100, workspace=torch.empty(max(need - 1, 1), dtype=torch.uint8, device=DEV))
+    with pytest.raises(ValueError):
+        attn.decode(q, kc, vc, bt, sl, 100, out=torch.empty(B, H, Lq + 1, d, dtype=torch.float16, device=DEV))
+    out, lse = attn.decode(q, kc, vc, bt, sl, 100)  # and the defaults still work
+    torch.cuda.synchronize(DEV)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()

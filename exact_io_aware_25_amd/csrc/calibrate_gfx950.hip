@@ -14,6 +14,10 @@
 //       then the cost of single instructions (8 independent chains per
 //       wave) with 1 and 4 waves per SIMD, and 4 MFMAs with 16 independent
 //       FMAs of the same wave between them.
+//   calibrate_gfx950 --fp8acc  how exactly one v_mfma_scale_f32_32x32x64_f8f6f4
+//       (E4M3, unit scales) sums its 64 products: its 32x32 results against
+//       the exact sums, for small random values, for one large product among
+//       small ones, and for two large products that cancel.
 //   calibrate_gfx950 --read    HBM read rate of a plain kernel over 3.3 GB,
 //       the data read in 4 KiB blocks in order and in a random order (the
 //       access pattern of a paged KV cache).
@@ -21,6 +25,7 @@
 // Every memory access stays inside the buffers it is given.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -400,6 +405,95 @@ static int run_rates()
     return rc;
 }
 
+// ------------------------------------------------------------------ fp8 MFMA sums
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// One wave: lane l holds 32 E4M3 bytes of A row l%32 and of B column l%32 (k
+// bytes 32*(l/32)..+31 of each; the instruction pairs A and B bytes by lane
+// half and byte position), C = 0; result register r of lane l is
+// C[8*(r/4) + 4*(l/32) + r%4][l%32].
+__global__ void fp8_mfma_once(const i32x8 *a, const i32x8 *b, float *c)
+{
+    const int lane = threadIdx.x;
+    const f32x16 r = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[lane], b[lane], f32x16{}, 0, 0, 0, 127, 0, 127);
+    for (int i = 0; i < 16; ++i) c[lane * 16 + i] = r[i];
+}
+
+static double e4m3_value(unsigned char x)
+{
+    const int sgn = x >> 7, e = (x >> 3) & 15, m = x & 7;
+    const double v = e == 0 ? m * std::ldexp(1.0, -9) : (8 + m) * std::ldexp(1.0, e - 10);
+    return sgn ? -v : v;
+}
+
+static unsigned char e4m3_nearest(double v)  // by search: exact for the values used here
+{
+    unsigned char best = 0;
+    for (int x = 0; x < 256; ++x) {
+        if ((x & 0x7f) == 0x7f) continue;  // NaN patterns
+        if (std::fabs(e4m3_value((unsigned char)x) - v) < std::fabs(e4m3_value(best) - v)) best = (unsigned char)x;
+    }
+    return best;
+}
+
+static int run_fp8acc()
+{
+    unsigned long long st = 77;
+    auto uni = [&]() {
+        st = st * 6364136223846793005ULL + 1442695040888963407ULL;
+        return ((st >> 11) + 0.5) * (1.0 / 9007199254740992.0);
+    };
+    std::vector<unsigned char> A(64 * 32), Bm(64 * 32);  // lane-major: lane l's 32 bytes
+    i32x8 *da, *db;
+    float *dc;
+    CHECK_HIP(hipMalloc(&da, 64 * sizeof(i32x8)));
+    CHECK_HIP(hipMalloc(&db, 64 * sizeof(i32x8)));
+    CHECK_HIP(hipMalloc(&dc, 64 * 16 * sizeof(float)));
+    const char *names[3] = {"random |x| < 1", "one product 240*6 among small ones", "240*6 - 240*6 among small ones"};
+    for (int cs = 0; cs < 3; ++cs) {
+        for (int l = 0; l < 64; ++l)
+            for (int k = 0; k < 32; ++k) {
+                A[l * 32 + k] = e4m3_nearest((uni() - 0.5) * 1.0);
+                Bm[l * 32 + k] = e4m3_nearest((uni() - 0.5) * 1.0);
+            }
+        if (cs >= 1)
+            for (int l = 0; l < 32; ++l) {  // byte 0 of lane half 0 of every row and column
+                A[l * 32] = e4m3_nearest(240.0);
+                Bm[l * 32] = e4m3_nearest(6.0);
+                if (cs == 2) {  // and byte 0 of lane half 1: -240 * 6
+                    A[(l + 32) * 32] = e4m3_nearest(-240.0);
+                    Bm[(l + 32) * 32] = e4m3_nearest(6.0);
+                }
+            }
+        CHECK_HIP(hipMemcpy(da, A.data(), A.size(), hipMemcpyHostToDevice));
+        CHECK_HIP(hipMemcpy(db, Bm.data(), Bm.size(), hipMemcpyHostToDevice));
+        hipLaunchKernelGGL(fp8_mfma_once, dim3(1), dim3(64), 0, 0, da, db, dc);
+        CHECK_HIP(hipDeviceSynchronize());
+        std::vector<float> c(64 * 16);
+        CHECK_HIP(hipMemcpy(c.data(), dc, c.size() * sizeof(float), hipMemcpyDeviceToHost));
+        double max_err = 0, max_mag = 0;
+        for (int l = 0; l < 64; ++l)
+            for (int r = 0; r < 16; ++r) {
+                const int row = 8 * (r / 4) + 4 * (l / 32) + r % 4, col = l % 32;
+                double exact = 0, mag = 0;
+                for (int h = 0; h < 2; ++h)
+                    for (int k = 0; k < 32; ++k) {
+                        const double t = e4m3_value(A[(row + 32 * h) * 32 + k]) * e4m3_value(Bm[(col + 32 * h) * 32 + k]);
+                        exact += t;
+                        mag = std::max(mag, std::fabs(t));
+                    }
+                max_err = std::max(max_err, std::fabs((double)c[l * 16 + r] - exact));
+                max_mag = std::max(max_mag, mag);
+            }
+        std::printf("fp8 MFMA, %-36s largest |product| %8.3f, max |result - exact sum| %.3e (%.2e of it)\n",
+                    names[cs], max_mag, max_err, max_err / max_mag);
+    }
+    CHECK_HIP(hipFree(da));
+    CHECK_HIP(hipFree(db));
+    CHECK_HIP(hipFree(dc));
+    return 0;
+}
+
 // ------------------------------------------------------------------ HBM read rate
 // Wave w reads 4 KiB blocks order[w*per .. w*per+per-1] (entries past nblk
 // are skipped), 16 bytes per lane per load; one word per lane is written.
@@ -475,6 +569,7 @@ int main(int argc, char **argv)
     if (std::strcmp(mode, "--check") == 0) return run_checks();
     if (std::strcmp(mode, "--rates") == 0) return run_rates();
     if (std::strcmp(mode, "--read") == 0) return run_read();
-    std::printf("usage: %s --check | --rates | --read\n", argv[0]);
+    if (std::strcmp(mode, "--fp8acc") == 0) return run_fp8acc();
+    std::printf("usage: %s --check | --rates | --read | --fp8acc\n", argv[0]);
     return 2;
 }

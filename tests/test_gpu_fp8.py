@@ -15,6 +15,17 @@ R is obtained from the oracle itself: sum_j P_ij^2 v_jc^2 =
 exp(lse2_i - 2 lse_i) * O2_ic, where (O2, lse2) is attention with the scores
 doubled (scale 2s) and the values squared (v^2 of an E4M3 value is exact in
 fp16, as are the E4M3 inputs widened to fp16).
+
+The scores carry one more error: the fp8 MFMA sums its 64 products to about
+12 bits relative to the largest of them (measured by calibrate_gfx950
+--fp8acc: up to 2.6e-4 of the largest product; 2^-11 is taken, twice that),
+so a score of row i is off by at most s_err_i = scale * (d/64) * 2^-11 * M_i,
+with M_i = max_c |q_ic| * max |k| bounding every product of the row.  A
+shift of every weight by at most e^(s_err) moves lse by at most s_err and
+O_ic by at most s_err * sum_j P_ij |v_jc - O_ic| <= 2 s_err max|v|: both
+are added to the bounds.  (On N(0,1) data the term is ~1e-3 and the observed
+errors stay ~50 times below it; it matters for rows whose scores reach the
+hundreds.)
 """
 import math
 
@@ -31,29 +42,40 @@ pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda:0")
 U8 = 2.0 ** -4
+EPS8 = 2.0 ** -11  # one fp8 MFMA's sum against the largest product (2x the measured worst)
 
 
 def fp8_bound_inputs(q, k, v, causal, window, scale, rows=None):
-    """Oracle O, lse and the per-element R of the fp8 inputs (rows optional)."""
+    """Oracle O, lse, the per-element R of the fp8 inputs (rows optional), and
+    (s_err, o_err): the per-row bounds of the MFMA's score error on lse and O."""
     q16, k16, v16 = (t.to(torch.float16) for t in (q, k, v))
     o, lse = oracle.attention(q16, k16, v16, "f16", causal, window, scale, rows=rows)
     o2, lse2 = oracle.attention(q16, k16, v16 * v16, "f16", causal, window, 2 * scale, rows=rows)
     r = np.sqrt(np.maximum(o2, 0.0) * np.exp(lse2 - 2 * lse)[..., None])
-    return o, lse, r
+    d = q.shape[-1]
+    qrows = q.float().numpy().reshape(-1, d)
+    if rows is not None:
+        qrows = qrows[np.asarray(rows)]
+    m = np.abs(qrows).max(axis=1) * float(k.float().abs().max())
+    s_err = (scale * (d // 64) * EPS8 * m).reshape(lse.shape)
+    o_err = 2.0 * s_err * float(v.float().abs().max())
+    return o, lse, r, (s_err, o_err)
 
 
-def check_fp8(out, lse, ref_o, ref_lse, r, case):
+def check_fp8(out, lse, ref_o, ref_lse, r, case, score_err):
+    s_err, o_err = score_err
     o = out.double().numpy().reshape(ref_o.shape)
     l = lse.double().numpy().reshape(ref_lse.shape)
     assert np.isfinite(o).all() and np.isfinite(l).all(), f"{case}: non-finite output"
     floor = np.abs(torch.from_numpy(ref_o).to(torch.bfloat16).double().numpy() - ref_o)
-    bound = floor + 6 * (U8 / math.sqrt(3)) * r + 2.0 ** -12
+    bound = floor + 6 * (U8 / math.sqrt(3)) * r + 2.0 ** -12 + o_err[..., None]
     err = np.abs(o - ref_o)
     worst = np.unravel_index(np.argmax(err - bound), err.shape)
     assert (err <= bound).all(), (f"{case}: error {err[worst]:.3e} > bound {bound[worst]:.3e} at {worst} "
                                   f"(exact {ref_o[worst]:.4e}, R {r[worst]:.3e})")
     lerr = float(np.abs(l - ref_lse).max())
-    assert lerr <= LSE_TOL, f"{case}: max|dlse| = {lerr:.3e}"
+    lworst = float((np.abs(l - ref_lse) - (LSE_TOL + s_err)).max())
+    assert lworst <= 0, f"{case}: max|dlse| = {lerr:.3e} exceeds 1e-3 + the score-error bound by {lworst:.3e}"
     print(f"  {case}: max|dO| {err.max():.3e}, max error/bound {(err / bound).max():.3f}, max|dlse| {lerr:.2e}",
           flush=True)
     return float(err.max()), float((err / bound).max())
@@ -76,8 +98,8 @@ def test_fp8_small_grid(d, causal):
                 out, lse = attn.forward(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, window=window)
                 torch.cuda.synchronize()
                 scale = oracle.resolve_scale(0.0, d)
-                ref_o, ref_l, r = fp8_bound_inputs(q, k, v, causal, window, scale)
-                check_fp8(out.cpu(), lse.cpu(), ref_o, ref_l, r, case)
+                ref_o, ref_l, r, se = fp8_bound_inputs(q, k, v, causal, window, scale)
+                check_fp8(out.cpu(), lse.cpu(), ref_o, ref_l, r, case, se)
 
 
 @pytest.mark.parametrize("name", ["fp8_fa3_4k", "fp8_causal_128k_h4"])
@@ -88,8 +110,8 @@ def test_fp8_workload_sampled(name):
     out, lse = attn.forward(q.to(DEV), k.to(DEV), v.to(DEV), causal=w.causal, window=w.window, scale=w.scale)
     torch.cuda.synchronize()
     rows = sample_rows(w.B, w.H, w.L, 24, seed=17)
-    ref_o, ref_l, r = fp8_bound_inputs(q, k, v, w.causal, w.window, w.scale, rows=rows)
-    check_fp8(out.cpu().reshape(-1, w.d)[rows], lse.cpu().reshape(-1)[rows], ref_o, ref_l, r, name)
+    ref_o, ref_l, r, se = fp8_bound_inputs(q, k, v, w.causal, w.window, w.scale, rows=rows)
+    check_fp8(out.cpu().reshape(-1, w.d)[rows], lse.cpu().reshape(-1)[rows], ref_o, ref_l, r, name, se)
 
 
 def test_fp8_single_key_is_exact():

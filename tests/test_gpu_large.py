@@ -94,8 +94,8 @@ def test_fp8_forward_beyond_2_31():
         case = f"large fp8 forward, head {bh}"
         announce(case)
         rows = sample_rows(1, 1, L, 16, seed=bh)
-        ref_o, ref_l, r = fp8_bound_inputs(head(q, bh), head(k, bh), head(v, bh), True, -1, SCALE, rows=rows)
-        check_fp8(head(out, bh).reshape(-1, D)[rows], head(lse, bh).reshape(-1)[rows], ref_o, ref_l, r, case)
+        ref_o, ref_l, r, se = fp8_bound_inputs(head(q, bh), head(k, bh), head(v, bh), True, -1, SCALE, rows=rows)
+        check_fp8(head(out, bh).reshape(-1, D)[rows], head(lse, bh).reshape(-1)[rows], ref_o, ref_l, r, case, se)
     del q, k, v, out, lse
     torch.cuda.empty_cache()
 

@@ -7,10 +7,14 @@
 //       * v_permlane32_swap(x, x): first result = x of lane l%32, second =
 //         x of lane l%32 + 32;
 //       * buffer_load_dwordx4 ... lds: lane i's 16 bytes land at M0 + 16*i,
-//         read from lane i's own offset, and out-of-range lanes write zeros.
+//         read from lane i's own offset, and out-of-range lanes write zeros;
+//       and reports (without failing) which SIMD each wave of an 8-wave
+//       workgroup runs on (HW_REG_HW_ID bits 5:4): --rates places its two
+//       wave roles on shared SIMDs by assuming waves w and w+4 share one.
 //   calibrate_gfx950 --rates   issue rates per SIMD, no memory traffic:
 //       MFMA 32x32x16 f16 alone, the softmax VALU mix of one 64-key tile
-//       alone, both in one wave, and one MFMA wave beside one VALU wave;
+//       alone, both in one wave, and one MFMA wave beside one VALU wave on
+//       every SIMD;
 //       then the cost of single instructions (8 independent chains per
 //       wave) with 1 and 4 waves per SIMD, and 4 MFMAs with 16 independent
 //       FMAs of the same wave between them.
@@ -45,6 +49,14 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+// ------------------------------------------------------------------ wave placement
+// SIMD of each wave of the workgroup: HW_REG_HW_ID (register 4), bits 5:4.
+__global__ void simd_of_wave(int *out)
+{
+    const unsigned simd = __builtin_amdgcn_s_getreg((1 << 11) | (4 << 6) | 4);
+    if (threadIdx.x % 64 == 0) out[blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64] = (int)simd;
+}
 
 // ------------------------------------------------------------------ layout checks
 // One wave.  lds holds 1024 shorts; lane addresses stay below 2 KiB - 8 bytes.
@@ -144,6 +156,22 @@ static int run_checks()
         std::printf("buffer_load ... lds placement (%d-byte range): %s\n", records,
                     failures > before ? "MISMATCH" : "ok");
     }
+    // wave placement (reported, not checked): 16 workgroups of 8 waves
+    hipLaunchKernelGGL(simd_of_wave, dim3(16), dim3(512), 0, 0, d_i);
+    CHECK_HIP(hipDeviceSynchronize());
+    CHECK_HIP(hipMemcpy(hi.data(), d_i, 128 * sizeof(int), hipMemcpyDeviceToHost));
+    bool pairs = true;
+    for (int b = 0; b < 16; ++b) {
+        int seen = 0;
+        for (int w = 0; w < 4; ++w) {
+            pairs = pairs && hi[8 * b + w] == hi[8 * b + w + 4];
+            seen |= 1 << hi[8 * b + w];
+        }
+        pairs = pairs && seen == 15;
+    }
+    std::printf("wave placement, workgroup 0, SIMD of waves 0..7: %d %d %d %d %d %d %d %d; waves w and w+4 "
+                "share a SIMD, waves 0..3 on four SIMDs, in all 16 workgroups: %s\n",
+                hi[0], hi[1], hi[2], hi[3], hi[4], hi[5], hi[6], hi[7], pairs ? "yes" : "NO");
     CHECK_HIP(hipFree(d_s));
     CHECK_HIP(hipFree(d_i));
     CHECK_HIP(hipFree(d_src));
@@ -156,7 +184,9 @@ static int run_checks()
 // MODE 0: 16 MFMA per iteration (4 independent accumulators)
 // MODE 1: softmax VALU mix of one wave-tile (32 fma+exp2, 16 cvt, 16 dot2)
 // MODE 2: both, in every wave
-// MODE 3: even waves MFMA only, odd waves VALU only
+// MODE 3: the first half of the waves MFMA only, the second half VALU only
+//         (waves w and w+4 share a SIMD, so at 2 waves per SIMD every SIMD
+//         holds one wave of each kind)
 template <int MODE>
 __global__ void rates(float *out, int iters, long long *cycles)
 {
@@ -172,8 +202,9 @@ __global__ void rates(float *out, int iters, long long *cycles)
         s1[i] = -i * 1e-2f;
     }
     float acc = 0.f;
-    const bool do_mfma = MODE == 0 || MODE == 2 || (MODE == 3 && (wave & 1) == 0);
-    const bool do_valu = MODE == 1 || MODE == 2 || (MODE == 3 && (wave & 1) == 1);
+    const bool first_half = wave < (int)blockDim.x / 128;
+    const bool do_mfma = MODE == 0 || MODE == 2 || (MODE == 3 && first_half);
+    const bool do_valu = MODE == 1 || MODE == 2 || (MODE == 3 && !first_half);
     const long long t0 = clock64();
     for (int it = 0; it < iters; ++it) {
         if (do_mfma) {
@@ -208,7 +239,7 @@ __global__ void rates(float *out, int iters, long long *cycles)
     float r = acc;
     for (int i = 0; i < 16; ++i) r += c0[i] + c1[i] + c2[i] + c3[i] + s0[i] + s1[i];
     out[blockIdx.x * blockDim.x + threadIdx.x] = r;
-    if (threadIdx.x == 0 && blockIdx.x == 0) cycles[0] = t1 - t0;
+    if (threadIdx.x % 64 == 0 && blockIdx.x == 0) cycles[threadIdx.x / 64] = t1 - t0;  // every wave of block 0
 }
 
 template <int MODE>
@@ -225,12 +256,15 @@ static int time_mode(const char *name, int waves_per_simd, int cus, float *out, 
     CHECK_HIP(hipEventSynchronize(e1));
     float ms = 0;
     CHECK_HIP(hipEventElapsedTime(&ms, e0, e1));
-    long long c = 0;
-    CHECK_HIP(hipMemcpy(&c, cyc, sizeof c, hipMemcpyDeviceToHost));
+    long long c[16] = {};
+    CHECK_HIP(hipMemcpy(c, cyc, sizeof c, hipMemcpyDeviceToHost));
     const double mfma_waves = MODE == 0 || MODE == 2 ? threads / 64.0 : (MODE == 3 ? threads / 128.0 : 0.0);
     const double tflops = mfma_waves * 16 * 32768.0 * iters * cus / (ms * 1e-3) / 1e12;
-    std::printf("%-44s waves/SIMD %d  %8.3f ms  %7.1f clocks/iteration (wave 0)  MFMA %7.1f TFLOP/s\n", name,
-                waves_per_simd, ms, (double)c / iters, tflops);
+    std::printf("%-44s waves/SIMD %d  %8.3f ms  %7.1f clocks/iteration (wave 0)  MFMA %7.1f TFLOP/s", name,
+                waves_per_simd, ms, (double)c[0] / iters, tflops);
+    // MODE 3: wave 0 runs MFMAs, wave threads/128 (on the same SIMD) the VALU mix
+    if (MODE == 3) std::printf("  VALU wave %7.1f clocks/iteration", (double)c[threads / 128] / iters);
+    std::printf("\n");
     CHECK_HIP(hipEventDestroy(e0));
     CHECK_HIP(hipEventDestroy(e1));
     return 0;
@@ -390,7 +424,7 @@ static int run_rates()
     rc |= time_mode<1>("softmax VALU mix of one 64-key tile", 4, cus, out, cyc);
     rc |= time_mode<2>("both in every wave", 1, cus, out, cyc);
     rc |= time_mode<2>("both in every wave", 2, cus, out, cyc);
-    rc |= time_mode<3>("MFMA-only wave beside VALU-only wave", 2, cus, out, cyc);
+    rc |= time_mode<3>("MFMA-only wave beside VALU-only wave, one SIMD", 2, cus, out, cyc);
     rc |= time_mfma_random(1, cus, out, cyc);
     rc |= time_mfma_random(2, cus, out, cyc);
     for (int w : {1, 4}) {

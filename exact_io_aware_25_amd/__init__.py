@@ -146,6 +146,7 @@ def attn_resolve_scale(scale: float, d: int) -> float:
 def attn_launch_shape(B, H, L, d, causal, window):
     """(waves per key-range group, key-range groups) attn_fwd would use; raises on bad arguments."""
     waves, splits = ctypes.c_int(), ctypes.c_int()
+    B, H, L, d, window = _int32(B=B, H=H, L=L, d=d, window=window)
     st = library().attn_launch_shape(B, H, L, d, int(causal), window, ctypes.byref(waves), ctypes.byref(splits))
     if st != ATTN_OK:
         raise ValueError(attn_status_string(st))
@@ -190,12 +191,25 @@ def forward(q, k, v, causal: bool = False, window: int = -1, scale=None, out=Non
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     fn = {torch.float16: attn_fwd, torch.bfloat16: attn_fwd_bf16, torch.float8_e4m3fn: attn_fwd_fp8}[q.dtype]
+    B, H, H_kv, L, d, window = _int32(B=B, H=H, H_kv=H_kv, L=L, d=d, window=window)
     with torch.cuda.device(q.device):
         status = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                     B, H, H_kv, L, d, int(bool(causal)), int(window),
                     0.0 if scale is None else float(scale), stream.cuda_stream)
     _check(status)
     return out, lse
+
+
+def _int32(**values):
+    """The given integers, checked to fit the C ABI's 32-bit int arguments.
+
+    ctypes would otherwise pass an out-of-range Python int wrapped modulo
+    2^32, which could turn an invalid argument into a valid but different one.
+    """
+    for name, value in values.items():
+        if not -2 ** 31 <= int(value) < 2 ** 31:
+            raise ValueError(f"{name}={value} does not fit a 32-bit int argument")
+    return tuple(int(v) for v in values.values())
 
 
 def _check(status):
@@ -249,6 +263,7 @@ def backward(q, k, v, out, lse, dout, causal: bool = False, window: int = -1, sc
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     fn = attn_bwd if q.dtype == torch.float16 else attn_bwd_bf16
+    B, H, H_kv, L, d, window = _int32(B=B, H=H, H_kv=H_kv, L=L, d=d, window=window)
     with torch.cuda.device(q.device):
         status = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
                     dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), B, H, H_kv, L, d,
@@ -293,6 +308,9 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int, window:
     if (tuple(lse.shape) != (B, H, Lq) or lse.dtype != torch.float32 or not lse.is_contiguous()
             or lse.device != q.device):
         raise ValueError("lse must be a contiguous float32 tensor [B, H, Lq] on q's device")
+    B, H, H_kv, Lq, d, block_size, max_blocks, num_blocks, max_seq_len, window = _int32(
+        B=B, H=H, H_kv=H_kv, Lq=Lq, d=d, block_size=block_size, max_blocks=block_table.shape[1],
+        num_blocks=num_blocks, max_seq_len=max_seq_len, window=window)
     need = attn_decode_workspace_size(B, H, H_kv, Lq, d, max_seq_len)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
@@ -305,7 +323,7 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int, window:
     with torch.cuda.device(q.device):
         status = fn(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
                     seq_lens.data_ptr(), out.data_ptr(), lse.data_ptr(), workspace.data_ptr(), B, H, H_kv, Lq, d,
-                    block_size, block_table.shape[1], num_blocks, int(max_seq_len), int(window),
+                    block_size, max_blocks, num_blocks, max_seq_len, window,
                     0.0 if scale is None else float(scale), stream.cuda_stream)
     _check(status)
     return out, lse

@@ -119,6 +119,12 @@ def test_launch_shape():
                     assert not (waves == 8 and splits == 2 and d == 128)
     with pytest.raises(ValueError):
         shape(1, 4, 100, 96, True, -1)
+    # 2^32 - 1 would reach the library as -1 (no window) if passed through
+    # ctypes unchecked; 2^31 as a negative L
+    with pytest.raises(ValueError, match="32-bit"):
+        shape(1, 4, 100, 64, True, 2 ** 32 - 1)
+    with pytest.raises(ValueError, match="32-bit"):
+        shape(1, 4, 2 ** 31, 64, True, -1)
     with pytest.raises(ValueError):
         shape(1, 4, 100, 64, 2, -1)
 

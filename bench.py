@@ -114,6 +114,7 @@ def time_workload(w, steps: int, warmup: int):
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats(dev)
     base = torch.cuda.memory_allocated(dev)
+    free_before = torch.cuda.mem_get_info(dev)[0]
     out = torch.empty(q.shape, dtype=torch.bfloat16 if w.dtype == "f8" else q.dtype, device=dev)
     lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -121,20 +122,24 @@ def time_workload(w, steps: int, warmup: int):
         attn.forward(q, k, v, causal=w.causal, window=w.window, scale=w.scale, out=out, lse=lse,
                      stream=stream)
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
+    # one event between consecutive launches: the first and last bracket the
+    # timed region (its mean is the step time), the others give each launch
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(steps):
+    events[0].record(stream)
+    for i in range(steps):
         attn.forward(q, k, v, causal=w.causal, window=w.window, scale=w.scale, out=out, lse=lse,
                      stream=stream)
-    stop.record(stream)
+        events[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = start.elapsed_time(stop) / steps
+    ms = events[0].elapsed_time(events[-1]) / steps
+    per_launch = sorted(events[i].elapsed_time(events[i + 1]) for i in range(steps))
     peak = torch.cuda.max_memory_allocated(dev)
-    return dict(ms=ms, wall_s=wall, out=out, lse=lse, inputs=(q, k, v),
-                peak_mem=peak, peak_mem_incl_inputs=peak, peak_mem_call=peak - base)
+    free_after = torch.cuda.mem_get_info(dev)[0]
+    return dict(ms=ms, ms_median=per_launch[len(per_launch) // 2], ms_min=per_launch[0], wall_s=wall,
+                out=out, lse=lse, inputs=(q, k, v), peak_mem=peak, peak_mem_incl_inputs=peak,
+                peak_mem_call=peak - base, device_free_delta=free_before - free_after)
 
 
 def data_sensitivity(w, inputs, steps: int):
@@ -411,6 +416,17 @@ def roofline_block(w, ms):
             "traffic": profiled_traffic(w, "attn_fwd", source)}
 
 
+def write_csv(path, header, rows):
+    """The results file of the pages' benchmark assignment: one row per
+    length with time and peak memory, "OOM" where a run ran out of memory."""
+    import csv
+    with open(path, "w", newline="") as f:
+        wr = csv.writer(f)
+        wr.writerow(header)
+        wr.writerows(rows)
+    print(f"bench.py: wrote {len(rows)} rows to {path}", file=sys.stderr, flush=True)
+
+
 def loglog_slope(xs, ys):
     lx, ly = np.log(np.asarray(xs, float)), np.log(np.asarray(ys, float))
     return float(np.polyfit(lx, ly, 1)[0])
@@ -434,6 +450,9 @@ def main():
                     help="time the paged decode (attn_decode) on a decode workload")
     ap.add_argument("--compare", action="store_true",
                     help="time the kernel beside standard attention over the pages' length sweep")
+    ap.add_argument("--csv", default=None,
+                    help="with --sweep or --compare, also write the per-length results (L, time_ms, mem_GB, "
+                         "'OOM' where standard attention ran out of memory) to this CSV file")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (attn_bwd) on the workload instead of the forward")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -485,7 +504,9 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "H_kv": w.H_kv, "L": w.L, "d": w.d,
                    "causal": w.causal, "window": w.window, "scale": w.scale,
                    "algorithmic_flops": flops, "pct_of_mfma_peak": round(100 * tflops / mfma_peak(w), 2),
+                   "ms_median": round(r["ms_median"], 4), "ms_min": round(r["ms_min"], 4),
                    "peak_mem_bytes": r["peak_mem"], "peak_mem_call_bytes": r["peak_mem_call"],
+                   "device_free_delta_bytes": r["device_free_delta"],
                    "algorithmic_bytes": algorithmic_bytes(w)},
         "roofline": roofline_block(w, r["ms"]),
     }
@@ -504,6 +525,7 @@ def main():
             rs = time_workload(ws, max(5, args.steps), 3)
             f = algorithmic_flops(ws)
             rec = {"workload": name, "dtype": ws.dtype, "L": ws.L, "ms": round(rs["ms"], 4),
+                   "ms_median": round(rs["ms_median"], 4), "ms_min": round(rs["ms_min"], 4),
                    "tflops": round(f / (rs["ms"] * 1e-3) / 1e12, 2),
                    "pct_peak": round(100 * f / (rs["ms"] * 1e-3) / 1e12 / mfma_peak(ws), 2),
                    "peak_mem_bytes": rs["peak_mem"], "peak_mem_call_bytes": rs["peak_mem_call"],
@@ -521,6 +543,11 @@ def main():
                                            "slope_time": round(loglog_slope(Ls, ts), 3),
                                            "slope_memory": round(loglog_slope(Ls, ms_), 3)}}),
               file=sys.stderr, flush=True)
+        if args.csv:
+            write_csv(args.csv, ["workload", "dtype", "L", "time_ms", "time_ms_median", "time_ms_min", "mem_GB",
+                                 "tflops", "pct_peak"],
+                      [[r["workload"], r["dtype"], r["L"], r["ms"], r["ms_median"], r["ms_min"],
+                        round(r["peak_mem_bytes"] / 1e9, 6), r["tflops"], r["pct_peak"]] for r in sweep])
 
 
 def standard_attention(q, k, v, causal: bool, scale: float, rows_per_step: int = 8192,
@@ -623,6 +650,16 @@ def main_compare(args):
         r = compare_one(B, H, L, d, causal, 0.125, 3000 + i)
         rows.append(r)
         print(json.dumps({"compare": r}), flush=True)
+    if args.csv:
+        def std(r, key, scale=1.0):
+            v = r.get(key)
+            return "OOM" if r.get("standard_peak_bytes") == "OOM" else (round(v / scale, 6) if v is not None else "")
+        write_csv(args.csv, ["B", "H", "L", "d", "causal", "time_ms", "mem_GB", "standard_time_ms",
+                             "standard_mem_GB", "speedup", "memory_ratio"],
+                  [[r["B"], r["H"], r["L"], r["d"], int(r["causal"]), r["flash_ms"],
+                    round(r["flash_peak_bytes"] / 1e9, 6), std(r, "standard_ms"),
+                    std(r, "standard_peak_bytes", 1e9), r.get("speedup", ""), r.get("memory_ratio", "")]
+                   for r in rows])
     ok = [r for r in rows if r.get("standard_ms") and r.get("standard_result_valid")]
     print(json.dumps({"compare_summary": {
         "speedup_range": [min(r["speedup"] for r in ok), max(r["speedup"] for r in ok)],

@@ -159,11 +159,13 @@ def forward(q, k, v, causal: bool = False, window: int = -1, scale=None, out=Non
     float8_e4m3fn, on the GPU).
 
     Returns (out [B,H,L,d] of q's dtype -- bf16 for fp8 inputs --, lse [B,H,L] fp32).  ``scale=None``
-    selects 1/sqrt(d).  ``out``/``lse`` may be given to write into existing
+    selects 1/sqrt(d); an explicit scale must be finite and > 0 (ValueError
+    otherwise).  ``out``/``lse`` may be given to write into existing
     tensors.  Launches on ``stream`` (default: torch's current stream).
     """
     import torch
 
+    scale_value = _scale_arg(scale)
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D: [B, H, L, d] and [B, H_kv, L, d]")
     if (q.dtype not in (torch.float16, torch.bfloat16, torch.float8_e4m3fn) or k.dtype != q.dtype
@@ -195,9 +197,23 @@ def forward(q, k, v, causal: bool = False, window: int = -1, scale=None, out=Non
     with torch.cuda.device(q.device):
         status = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                     B, H, H_kv, L, d, int(bool(causal)), int(window),
-                    0.0 if scale is None else float(scale), stream.cuda_stream)
+                    scale_value, stream.cuda_stream)
     _check(status)
     return out, lse
+
+
+def _scale_arg(scale):
+    """The scale argument for the C ABI: None selects 1/sqrt(d) (passed as 0,
+    the ABI's request for the default); an explicit scale must be a finite
+    number > 0.  The ABI itself would silently replace a zero, negative or NaN
+    scale by the default, which would compute a different function than the
+    caller asked for, so the binding refuses them."""
+    if scale is None:
+        return 0.0
+    value = float(scale)
+    if not (value > 0.0 and value != float("inf")):
+        raise ValueError(f"scale must be None (1/sqrt(d)) or a finite number > 0, got {scale!r}")
+    return value
 
 
 def _int32(**values):
@@ -224,13 +240,15 @@ def backward(q, k, v, out, lse, dout, causal: bool = False, window: int = -1, sc
              dq=None, dk=None, dv=None, workspace=None, stream=None):
     """Gradients (dq, dk, dv) of attention for the upstream gradient ``dout``.
 
-    q, k, v, causal, window, scale as given to ``forward``; out and lse as it
+    q, k, v, causal, window, scale as given to ``forward`` (``scale=None``
+    selects 1/sqrt(d); an explicit scale must be finite and > 0); out and lse as it
     returned them; dout like out.  Outputs are allocated unless given;
     ``workspace`` (uint8, ``attn_bwd_workspace_size`` bytes) likewise.
     Launches on ``stream`` (default: torch's current stream).
     """
     import torch
 
+    scale_value = _scale_arg(scale)
     tensors = (q, k, v, out, dout)
     if any(t.dim() != 4 for t in tensors):
         raise ValueError("q, k, v, out, dout must be 4-D")
@@ -267,7 +285,7 @@ def backward(q, k, v, out, lse, dout, causal: bool = False, window: int = -1, sc
     with torch.cuda.device(q.device):
         status = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
                     dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), B, H, H_kv, L, d,
-                    int(bool(causal)), int(window), 0.0 if scale is None else float(scale), stream.cuda_stream)
+                    int(bool(causal)), int(window), scale_value, stream.cuda_stream)
     _check(status)
     return dq, dk, dv
 
@@ -278,12 +296,14 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int, window:
 
     q [B,H,Lq,d]; k_cache, v_cache [num_blocks,H_kv,block_size,d] (fp16 or
     bf16, on the GPU); block_table int32 [B, max_blocks]; seq_lens int32 [B]
-    on the GPU; ``max_seq_len`` bounds seq_lens (host int).  Returns (out
+    on the GPU; ``max_seq_len`` bounds seq_lens (host int); ``scale=None``
+    selects 1/sqrt(d), an explicit scale must be finite and > 0.  Returns (out
     [B,H,Lq,d], lse [B,H,Lq] fp32).  Launches on ``stream`` (default: torch's
     current stream).
     """
     import torch
 
+    scale_value = _scale_arg(scale)
     if q.dim() != 4 or k_cache.dim() != 4 or v_cache.dim() != 4:
         raise ValueError("q must be [B,H,Lq,d] and the caches [num_blocks,H_kv,block_size,d]")
     if q.dtype not in (torch.float16, torch.bfloat16) or k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
@@ -324,6 +344,6 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int, window:
         status = fn(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
                     seq_lens.data_ptr(), out.data_ptr(), lse.data_ptr(), workspace.data_ptr(), B, H, H_kv, Lq, d,
                     block_size, max_blocks, num_blocks, max_seq_len, window,
-                    0.0 if scale is None else float(scale), stream.cuda_stream)
+                    scale_value, stream.cuda_stream)
     _check(status)
     return out, lse

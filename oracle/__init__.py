@@ -64,7 +64,7 @@ def _bind(lib):
     lib.oracle_attn.argtypes = [u16p, u16p, u16p, ctypes.c_int,
                                 ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                 ctypes.c_int, ctypes.c_int, ctypes.c_float,
-                                i64p, ctypes.c_int64, f64p, f64p, ctypes.c_int]
+                                i64p, ctypes.c_int64, f64p, f64p, f64p, f64p, ctypes.c_int]
     lib.oracle_attn_bwd.restype = ctypes.c_int
     lib.oracle_attn_bwd.argtypes = [u16p, u16p, u16p, u16p, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -134,13 +134,17 @@ def resolve_scale(scale: float, d: int, lib=None) -> float:
 
 
 def attention(q, k, v, dtype: str, causal: bool, window: int = -1, scale: float = 0.0,
-              rows=None, threads: int = 0, lib=None):
+              rows=None, threads: int = 0, lib=None, with_abs: bool = False):
     """Exact attention of 16-bit inputs in fp64.
 
     q: [B,H,L,d]; k, v: [B,H_kv,L,d] (torch tensors or uint16 arrays of bit
     patterns).  ``rows``: optional flat row ids (b*H + h)*L + i; when given,
     the result holds those rows only, in that order.
     Returns (out, lse): fp64 [B,H,L,d] and [B,H,L], or [n, d] and [n].
+    With ``with_abs``, returns (out, lse, oabs, count, sabs): oabs shaped like
+    out holds sum_j P_ij |v_jc| (the softmax weights applied to |v|); count
+    and sabs shaped like lse hold each row's number of visible keys and
+    max_j scale * sum_c |q_ic k_jc|.
     """
     lib = lib or _default_lib()
     qb, kb, vb = _bits(q), _bits(k), _bits(v)
@@ -160,14 +164,21 @@ def attention(q, k, v, dtype: str, causal: bool, window: int = -1, scale: float 
         rows_ptr = _ptr(rows_arr, ctypes.c_int64)
     out = np.zeros((n, d), np.float64)
     lse = np.zeros((n,), np.float64)
+    oabs = np.zeros((n, d), np.float64) if with_abs else None
+    aux = np.zeros((n, 2), np.float64) if with_abs else None
     st = lib.oracle_attn(_ptr(qb, ctypes.c_uint16), _ptr(kb, ctypes.c_uint16), _ptr(vb, ctypes.c_uint16),
                          DTYPES[dtype], B, H, H_kv, L, d, int(bool(causal)), int(window), float(scale),
                          rows_ptr, n, _ptr(out, ctypes.c_double), _ptr(lse, ctypes.c_double),
-                         int(threads))
+                         _ptr(oabs, ctypes.c_double) if with_abs else None,
+                         _ptr(aux, ctypes.c_double) if with_abs else None, int(threads))
     if st != 0:
         raise ValueError(f"oracle_attn failed with status {st}")
     if rows is None:
-        return out.reshape(B, H, L, d), lse.reshape(B, H, L)
+        out, lse = out.reshape(B, H, L, d), lse.reshape(B, H, L)
+        if with_abs:
+            oabs, aux = oabs.reshape(B, H, L, d), aux.reshape(B, H, L, 2)
+    if with_abs:
+        return out, lse, oabs, aux[..., 0].copy(), aux[..., 1].copy()
     return out, lse
 
 

@@ -154,41 +154,57 @@ static int reads_kv_head(int64_t r, int b, int g, int H, int H_kv, int L)
  * (so O_i = acc / l).  qd: the row's decoded q; kd, vd: the decoded K/V head.
  * If dod (the row's decoded upstream gradient) is not NULL, also
  * D = dO_i . O_i for the backward pass, and rho = sqrt(sum_c (dO_ic O_ic)^2),
- * the root-sum-square of D's terms.  Returns 0, or -2 if the row sees no
- * key. */
+ * the root-sum-square of D's terms.  If acc_abs is not NULL it receives
+ * sum_j exp(s_ij - m) |v_jc| (the same weights, absolute values), and aux
+ * (2 doubles) the number of visible keys and max_j scale * sum_c |q_c k_jc|.
+ * Returns 0, or -2 if the row sees no key. */
 static int row_softmax(const double *qd, const double *dod, const double *kd, const double *vd,
                        int64_t i, int L, int d, int causal, int window, double sc,
                        double *s, double *acc, double *m_out, double *l_out, double *D_out,
-                       double *rho_out)
+                       double *rho_out, double *acc_abs, double *aux)
 {
-    double m = -INFINITY;
+    double m = -INFINITY, sabs = 0.0;
     int64_t count = 0;
     for (int64_t j = 0; j < L; ++j) {
         if (!oracle_visible(i, j, causal, window))
             continue;
-        double dot = 0.0;
-        for (int c = 0; c < d; ++c)
+        double dot = 0.0, dot_abs = 0.0;
+        for (int c = 0; c < d; ++c) {
             dot += qd[c] * kd[j * d + c];
+            dot_abs += fabs(qd[c] * kd[j * d + c]);
+        }
         s[j] = sc * dot;
         if (s[j] > m)
             m = s[j];
+        if (sc * dot_abs > sabs)
+            sabs = sc * dot_abs;
         ++count;
     }
     if (count == 0)
         return -2;
     double l = 0.0;
-    for (int c = 0; c < d; ++c)
+    for (int c = 0; c < d; ++c) {
         acc[c] = 0.0;
+        if (acc_abs)
+            acc_abs[c] = 0.0;
+    }
     for (int64_t j = 0; j < L; ++j) {
         if (!oracle_visible(i, j, causal, window))
             continue;
         double p = exp(s[j] - m);
         l += p;
-        for (int c = 0; c < d; ++c)
+        for (int c = 0; c < d; ++c) {
             acc[c] += p * vd[j * d + c];
+            if (acc_abs)
+                acc_abs[c] += p * fabs(vd[j * d + c]);
+        }
     }
     *m_out = m;
     *l_out = l;
+    if (aux) {
+        aux[0] = (double)count;
+        aux[1] = sabs;
+    }
     if (dod) {
         double D = 0.0, R = 0.0;
         for (int c = 0; c < d; ++c) {
@@ -208,13 +224,19 @@ static int row_softmax(const double *qd, const double *dod, const double *kd, co
  * rows: flat row ids r = (b*H + h)*L + i, or NULL for all B*H*L rows in
  *   order (then n_rows is ignored).
  * out: [n_rows, d] fp64, lse: [n_rows] fp64 (row order of `rows`).
+ * oabs: NULL, or [n_rows, d] fp64 receiving sum_j P_ij |v_jc| with P_ij the
+ *   softmax weights of the row (what a relative error of each weight can move
+ *   out[i,c] by, used by tests to bound 16-bit weight rounding).
+ * row_aux: NULL, or [n_rows, 2] fp64 receiving, per row, the number of
+ *   visible keys and max_j scale * sum_c |q_ic k_jc| (the size an absolute
+ *   error of the score sums can reach).
  * threads <= 0 uses OpenMP's default.
  * Returns 0, or -1 for bad arguments, or -2 if a row has no visible key.
  */
 int oracle_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v, int dtype,
                 int B, int H, int H_kv, int L, int d, int causal, int window,
                 float scale, const int64_t *rows, int64_t n_rows, double *out,
-                double *lse, int threads)
+                double *lse, double *oabs, double *row_aux, int threads)
 {
     if (B < 0 || H <= 0 || H_kv <= 0 || L < 0 || d <= 0 || H % H_kv != 0 || window < -1)
         return -1;
@@ -254,6 +276,7 @@ int oracle_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v, int dty
                 double *s = malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
                 double *qd = malloc(sizeof(double) * (size_t)d);
                 double *acc = malloc(sizeof(double) * (size_t)d);
+                double *acc_abs = malloc(sizeof(double) * (size_t)d);
 #pragma omp for schedule(dynamic, 8)
                 for (int64_t t = 0; t < n_rows; ++t) {
                     int64_t r = rows ? rows[t] : t;
@@ -264,18 +287,22 @@ int oracle_attn(const uint16_t *q, const uint16_t *k, const uint16_t *v, int dty
 
                     double m, l;
                     if (row_softmax(qd, NULL, kd, vd, i, L, d, causal, window, sc, s, acc, &m, &l,
-                                    NULL, NULL) != 0) {
+                                    NULL, NULL, oabs ? acc_abs : NULL, row_aux ? row_aux + 2 * t : NULL) != 0) {
 #pragma omp atomic write
                         status = -2;
                         continue;
                     }
-                    for (int c = 0; c < d; ++c)
+                    for (int c = 0; c < d; ++c) {
                         out[t * d + c] = acc[c] / l;
+                        if (oabs)
+                            oabs[t * d + c] = acc_abs[c] / l;
+                    }
                     lse[t] = m + log(l);
                 }
                 free(s);
                 free(qd);
                 free(acc);
+                free(acc_abs);
             }
         }
     }
@@ -407,7 +434,7 @@ int oracle_attn_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, con
                     if (!needed[r])
                         continue;
                     if (row_softmax(qd + r * d, dod + r * d, kd, vd, r % L, L, d, causal, window, sc,
-                                  s, acc, &m[r], &l[r], &Dr[r], &rho[r]) != 0) {
+                                  s, acc, &m[r], &l[r], &Dr[r], &rho[r], NULL, NULL) != 0) {
 #pragma omp atomic write
                         status = -2;
                     }

@@ -30,10 +30,12 @@ def mask_matrix(L: int, causal: bool, window: int) -> np.ndarray:
 
 
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, window: int,
-              scale: float):
+              scale: float, with_abs: bool = False):
     """fp64 attention. q: [B,H,L,d]; k, v: [B,H_kv,L,d] (float64 values).
 
-    Returns (out [B,H,L,d], lse [B,H,L]).
+    Returns (out [B,H,L,d], lse [B,H,L]); with ``with_abs`` also the weights
+    applied to |v| ([B,H,L,d]), the number of visible keys per row and
+    max_j scale * sum_c |q_ic k_jc| over the visible keys ([B,H,L] each).
     """
     B, H, L, d = q.shape
     H_kv = k.shape[1]
@@ -47,4 +49,11 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, window:
     total = weights.sum(axis=-1, keepdims=True)
     out = np.matmul(weights, v_full) / total
     lse = (row_max + np.log(total))[..., 0]
-    return out, lse
+    if not with_abs:
+        return out, lse
+    allowed = mask_matrix(L, causal, window)
+    oabs = np.matmul(weights, np.abs(v_full)) / total
+    count = np.broadcast_to(allowed.sum(axis=-1).astype(np.float64), (B, H, L))
+    score_abs = scale * np.matmul(np.abs(q), np.swapaxes(np.abs(k_full), -1, -2))
+    sabs = np.where(allowed, score_abs, -np.inf).max(axis=-1)
+    return out, lse, oabs, count, sabs

@@ -39,10 +39,13 @@ def gather_sequence(cache: np.ndarray, block_table: np.ndarray, b: int, g: int, 
 
 
 def decode_attention(q, k_cache, v_cache, block_table, seq_lens, dtype: str, window: int = -1,
-                     scale: float = 0.0, lib=None):
+                     scale: float = 0.0, lib=None, with_abs: bool = False):
     """q: [B, H, Lq, d]; caches: [num_blocks, H_kv, block_size, d] (16-bit
     patterns or torch tensors); block_table: int [B, max_blocks]; seq_lens:
-    int [B] (each >= Lq).  Returns (out [B, H, Lq, d], lse [B, H, Lq]) fp64."""
+    int [B] (each >= Lq).  Returns (out [B, H, Lq, d], lse [B, H, Lq]) fp64.
+    With ``with_abs`` also (oabs, count, sabs): the softmax weights applied
+    to |v| (shaped like out), and per query the number of visible keys and
+    max_j scale * sum_c |q_c k_jc| (shaped like lse)."""
     qd = oracle.decode(q, dtype, lib=lib)
     kbits = oracle._bits(k_cache)
     vbits = oracle._bits(v_cache)
@@ -56,6 +59,9 @@ def decode_attention(q, k_cache, v_cache, block_table, seq_lens, dtype: str, win
     group = H // H_kv
     out = np.zeros((B, H, Lq, d))
     lse = np.zeros((B, H, Lq))
+    oabs = np.zeros((B, H, Lq, d))
+    count = np.zeros((B, H, Lq))
+    sabs = np.zeros((B, H, Lq))
     for b in range(B):
         n = int(lens[b])
         if n < Lq:
@@ -73,4 +79,10 @@ def decode_attention(q, k_cache, v_cache, block_table, seq_lens, dtype: str, win
                     w = np.exp(s - m)
                     out[b, h, i] = (w @ vals[lo:p + 1]) / w.sum()
                     lse[b, h, i] = m + np.log(w.sum())
+                    if with_abs:
+                        oabs[b, h, i] = (w @ np.abs(vals[lo:p + 1])) / w.sum()
+                        count[b, h, i] = p + 1 - lo
+                        sabs[b, h, i] = sc * (np.abs(keys[lo:p + 1]) @ np.abs(qd[b, h, i])).max()
+    if with_abs:
+        return out, lse, oabs, count, sabs
     return out, lse

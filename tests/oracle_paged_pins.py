@@ -57,6 +57,14 @@ def pin_paged_vs_forward(mod):
         case = f"H={H}/{H_kv} n={n} d={d} Lq={Lq} window={window} {dtype} block={bs}"
         assert np.max(np.abs(o - fo[:, :, n - Lq:])) <= 1e-12, case
         assert np.max(np.abs(l - fl[:, :, n - Lq:])) <= 1e-12, case
+        # the weights applied to |v|, the visible-key count and the score bound
+        # against the C oracle's (themselves pinned against brute force)
+        _, _, oabs, cnt, sabs = mod.decode_attention(q[:, :, n - Lq:], kc, vc, bt, [n], dtype, window, scale,
+                                                     with_abs=True)
+        _, _, foabs, fcnt, fsabs = oracle.attention(q, k, v, dtype, True, window, scale, with_abs=True)
+        assert np.max(np.abs(oabs - foabs[:, :, n - Lq:])) <= 1e-12, case
+        assert np.array_equal(cnt, fcnt[:, :, n - Lq:]), case
+        assert np.max(np.abs(sabs - fsabs[:, :, n - Lq:])) <= 1e-12 * max(1.0, float(fsabs.max())), case
 
 
 def pin_paged_invariances(mod):

@@ -13,6 +13,9 @@ fix.  The checks are:
   the visible values and lse = ln(number of visible keys); identical value
   rows return that row; all-ones values return ones (softmax rows sum to 1);
   two visible keys give a sigmoid mix;
+* the per-element weights applied to |v|, visible-key counts and score bounds
+  (what the GPU tests derive rounding bounds from) against brute force and
+  closed forms (one key, two keys, nonnegative values, |O| bound);
 * invariances: adding a constant vector to every key, permuting keys and
   values together, doubling q vs doubling the scale, GQA vs K/V heads
   repeated to H, batch elements computed apart;
@@ -236,6 +239,65 @@ def pin_two_keys(lib):
     assert abs(lse[0, 0, 1] - (s0 + math.log1p(math.exp(s1 - s0)))) <= 1e-13
 
 
+# ---------------------------------------------------------------- weights applied to |v|
+def _run_abs(lib, q, k, v, dtype, causal, window, scale):
+    return oracle.attention(q, k, v, dtype, causal, window, scale, lib=lib, with_abs=True)
+
+
+def pin_abs_outputs_brute_force(lib):
+    """The weights applied to |v|, the visible-key count and the largest
+    scale * sum_c |q_ic k_jc| against whole-matrix NumPy on tiny shapes."""
+    for (B, H, H_kv, L, d, causal, window, dtype, seed) in [
+        (2, 4, 2, 17, 64, True, -1, "f16", 61), (1, 4, 1, 40, 128, False, 5, "bf16", 62),
+        (1, 2, 2, 65, 64, True, 9, "f16", 63), (2, 1, 1, 3, 64, False, -1, "bf16", 64),
+    ]:
+        q, k, v = make_qkv(B, H, H_kv, L, d, dtype, seed)
+        scale = 0.125 if d == 64 else float(np.float32(1 / math.sqrt(d)))
+        o, lse, oabs, count, sabs = _run_abs(lib, q, k, v, dtype, causal, window, scale)
+        bo, blse, boabs, bcount, bsabs = brute.attention(_f64(q), _f64(k), _f64(v), causal, window, scale,
+                                                         with_abs=True)
+        case = f"L={L} d={d} H={H}/{H_kv} causal={causal} window={window} {dtype}"
+        assert np.max(np.abs(oabs - boabs)) <= 1e-12, case
+        assert np.array_equal(count, bcount), case
+        assert np.max(np.abs(sabs - bsabs)) <= 1e-12 * max(1.0, float(np.max(bsabs))), case
+        o2, lse2 = _run(lib, q, k, v, dtype, causal, window, scale)
+        assert np.array_equal(o, o2) and np.array_equal(lse, lse2), case
+
+
+def pin_abs_outputs_closed_forms(lib):
+    """One visible key: the weights applied to |v| give |v_i|, one key is
+    counted and the score bound is scale * sum_c |q_ic k_ic|.  Two visible
+    keys (causal row 1): w |v_0| + (1 - w) |v_1| with the sigmoid weight w.
+    Nonnegative values: the weights applied to |v| equal O itself, and in
+    general they bound |O| (triangle inequality)."""
+    q, k, v = make_qkv(1, 4, 2, 40, 64, "f16", 65)
+    _, _, oabs, count, sabs = _run_abs(lib, q, k, v, "f16", True, 0, 0.125)
+    vd = np.repeat(_f64(v), 2, axis=1)
+    kd = np.repeat(_f64(k), 2, axis=1)
+    assert np.array_equal(oabs, np.abs(vd))
+    assert np.array_equal(count, np.ones_like(count))
+    want = 0.125 * np.einsum("bhid,bhid->bhi", np.abs(_f64(q)), np.abs(kd))
+    assert np.max(np.abs(sabs - want)) <= 1e-13 * np.max(want)
+
+    q, k, v = make_qkv(1, 1, 1, 2, 64, "bf16", 66)
+    o, _, oabs, count, sabs = _run_abs(lib, q, k, v, "bf16", True, -1, 0.125)
+    qd, kd, vd = _f64(q)[0, 0], _f64(k)[0, 0], _f64(v)[0, 0]
+    s0, s1 = 0.125 * float(qd[1] @ kd[0]), 0.125 * float(qd[1] @ kd[1])
+    w = 1.0 / (1.0 + math.exp(s1 - s0))
+    assert np.max(np.abs(oabs[0, 0, 1] - (w * np.abs(vd[0]) + (1 - w) * np.abs(vd[1])))) <= 1e-13
+    assert count[0, 0, 1] == 2 and count[0, 0, 0] == 1
+    want = 0.125 * max(float(np.abs(qd[1]) @ np.abs(kd[0])), float(np.abs(qd[1]) @ np.abs(kd[1])))
+    assert abs(sabs[0, 0, 1] - want) <= 1e-13 * want
+
+    q, k, v = make_qkv(1, 2, 1, 70, 64, "f16", 67)
+    for causal, window in [(True, -1), (False, 8)]:
+        o, _, oabs, count, _ = _run_abs(lib, q, k, v.abs().contiguous(), "f16", causal, window, 0.125)
+        assert np.max(np.abs(oabs - o)) <= 1e-13 * np.max(o)
+        o, _, oabs, _, _ = _run_abs(lib, q, k, v, "f16", causal, window, 0.125)
+        assert (oabs >= np.abs(o) * (1 - 1e-13)).all()
+        assert all(count[0, h, i] == visible_count(i, 70, causal, window) for h in range(2) for i in range(70))
+
+
 # ---------------------------------------------------------------- invariances
 def pin_key_shift(lib):
     """Adding c to every key row adds scale*q_i.c to every visible score of row i:
@@ -320,6 +382,6 @@ def pin_row_subset(lib):
 ALL_PINS = [
     pin_decoders_exhaustive, pin_f8_decoder_exhaustive, pin_f8_inputs_equal_their_f16_widening, pin_brute_force, pin_torch_sdpa, pin_single_visible_key,
     pin_causal_row0, pin_zero_keys, pin_identical_values, pin_ones, pin_two_keys,
-    pin_key_shift, pin_permutation, pin_scale_vs_query, pin_gqa_equals_repeated_heads,
+    pin_abs_outputs_brute_force, pin_abs_outputs_closed_forms, pin_key_shift, pin_permutation, pin_scale_vs_query, pin_gqa_equals_repeated_heads,
     pin_batch_independence, pin_default_scale, pin_row_subset,
 ]

@@ -226,3 +226,23 @@ def test_decode_workspace_size():
     assert ws(0, 4, 4, 1, 64, 100) == 0 and ws(1, 3, 2, 1, 64, 100) == 0 and ws(1, 4, 4, 1, 96, 100) == 0
     # partial results of every chunk: at least one (O, m, l) per query row
     assert ws(2, 8, 2, 3, 64, 100) >= 2 * 8 * 3 * (64 + 2) * 4
+
+
+def test_binding_refuses_explicit_bad_scale():
+    """An explicit scale must be finite and > 0: the C ABI would silently take
+    1/sqrt(d) for zero, negative or NaN values, a different function than the
+    one asked for.  None selects the default.  Checked before any tensor or
+    device check, so CPU tensors suffice."""
+    import math
+
+    import torch
+    assert attn._scale_arg(None) == 0.0
+    assert attn._scale_arg(0.125) == 0.125
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.float16)
+    for bad in (0.0, -0.125, math.nan, math.inf, -math.inf):
+        with pytest.raises(ValueError, match="scale"):
+            attn._scale_arg(bad)
+        with pytest.raises(ValueError, match="scale"):
+            attn.forward(q, q, q, scale=bad)
+        with pytest.raises(ValueError, match="scale"):
+            attn.backward(q, q, q, q, torch.zeros(1, 1, 4), q, scale=bad)

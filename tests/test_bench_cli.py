@@ -13,3 +13,15 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr and "--gpus 2" in r.stderr
     assert r.stdout.strip() == ""  # no JSON line
+
+
+def test_csv_results_file(tmp_path):
+    """The results file of the pages' benchmark assignment: a header, one row
+    per length, "OOM" kept as text."""
+    import csv
+
+    import bench
+    path = tmp_path / "sweep.csv"
+    bench.write_csv(str(path), ["L", "time_ms", "mem_GB"], [[4096, 0.03, 0.008], [131072, "OOM", "OOM"]])
+    rows = list(csv.reader(open(path)))
+    assert rows == [["L", "time_ms", "mem_GB"], ["4096", "0.03", "0.008"], ["131072", "OOM", "OOM"]]

@@ -28,10 +28,13 @@ def test_comparator_matches_oracle():
     q, k, v = workload_inputs(w)
     o = bench.standard_attention(q.to(DEV), k.to(DEV), v.to(DEV), True, w.scale)
     torch.cuda.synchronize()
-    ref, ref_lse = oracle.attention(q, k, v, "f16", True, -1, w.scale)
-    # the comparator rounds its scores and weights to fp16 (its own floor), so
-    # only the output bar applies; lse is not produced: pass the oracle's own
-    check(o.cpu(), torch.from_numpy(ref_lse), ref, ref_lse, "f16", "comparator", vmax=float(v.abs().max()))
+    ref = oracle.attention(q, k, v, "f16", True, -1, w.scale, with_abs=True)
+    # the comparator's own arithmetic: its fp16 product rounds each score
+    # q.k once (relative 2^-11, at most 2^-11 * sabs_i in natural-log units;
+    # the scale 1/8 is exact), and its softmax rounds each weight to fp16 (the
+    # u of the bound); lse is not produced: pass the oracle's own
+    check(o.cpu(), torch.from_numpy(ref[1]), ref, "f16", "comparator", vmax=float(v.abs().max()),
+          rel_extra=2.0 ** -11 * ref[4])
 
 
 def test_page_accuracy_check():

@@ -60,7 +60,7 @@ def test_forward_beyond_2_31(big16):
         announce(case)
         rows = sample_rows(1, 1, L, 24, seed=bh)
         ref_o, ref_l = oracle.attention(head(q, bh), head(k, bh), head(v, bh), "f16", True, -1, SCALE, rows=rows)
-        check(head(out, bh).reshape(-1, D)[rows], head(lse, bh).reshape(-1)[rows], ref_o, ref_l, "f16", case)
+        check(head(out, bh).reshape(-1, D)[rows], head(lse, bh).reshape(-1)[rows], (ref_o, ref_l), "f16", case)
 
 
 def test_backward_beyond_2_31(big16):
@@ -127,4 +127,4 @@ def test_decode_cache_beyond_2_31():
     small = torch.where(table >= 0, remap[table.clamp(min=0).long()], table)
     idx = used.to(DEV)
     ref_o, ref_l = paged.decode_attention(q.cpu(), kc[idx].cpu(), vc[idx].cpu(), small, lens, "bf16")
-    check(out.cpu(), lse.cpu(), ref_o, ref_l, "bf16", "large decode")
+    check(out.cpu(), lse.cpu(), (ref_o, ref_l), "bf16", "large decode")

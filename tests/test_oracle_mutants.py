@@ -32,6 +32,10 @@ MUTANTS = {
     "f8_bias": ("mag = ldexp((double)(8 + frac), expo - 10);", "mag = ldexp((double)(8 + frac), expo - 9);"),
     "f8_subnormal_exponent": ("mag = ldexp((double)frac, -9);", "mag = ldexp((double)frac, -10);"),
     "f8_top_exponent_is_nan": ("else if (expo == 15 && frac == 7)", "else if (expo == 15)"),
+    "abs_weights_signed": ("acc_abs[c] += p * fabs(vd[j * d + c]);", "acc_abs[c] += p * vd[j * d + c];"),
+    "abs_weights_unnormalised": ("oabs[t * d + c] = acc_abs[c] / l;", "oabs[t * d + c] = acc_abs[c];"),
+    "score_abs_signed": ("dot_abs += fabs(qd[c] * kd[j * d + c]);", "dot_abs += qd[c] * kd[j * d + c];"),
+    "visible_count_off_by_one": ("aux[0] = (double)count;", "aux[0] = (double)(count - 1);"),
     # backward pass
     "bwd_dq_uses_values": ("acc[c] += dS * kd[j * d + c];", "acc[c] += dS * vd[j * d + c];"),
     "bwd_dq_scale_dropped": ("dq[t * d + c] = sc * acc[c];", "dq[t * d + c] = acc[c];"),
@@ -83,6 +87,11 @@ PAGED_MUTANTS = {
     "paged_no_normalisation": ("out[b, h, i] = (w @ vals[lo:p + 1]) / w.sum()", "out[b, h, i] = w @ vals[lo:p + 1]"),
     "paged_lse_without_max": ("lse[b, h, i] = m + np.log(w.sum())", "lse[b, h, i] = np.log(w.sum())"),
     "paged_gqa_interleaved": ("for h in range(g * group, (g + 1) * group):", "for h in range(g, H, H_kv):"),
+    "paged_abs_weights_signed": ("oabs[b, h, i] = (w @ np.abs(vals[lo:p + 1])) / w.sum()",
+                                 "oabs[b, h, i] = (w @ vals[lo:p + 1]) / w.sum()"),
+    "paged_count_whole_sequence": ("count[b, h, i] = p + 1 - lo", "count[b, h, i] = n"),
+    "paged_score_abs_unscaled": ("sabs[b, h, i] = sc * (np.abs(keys[lo:p + 1]) @ np.abs(qd[b, h, i])).max()",
+                                 "sabs[b, h, i] = (np.abs(keys[lo:p + 1]) @ np.abs(qd[b, h, i])).max()"),
 }
 
 

@@ -80,6 +80,9 @@ __global__ __launch_bounds__(64 * NW * SPLIT) void attn_fwd_kernel(Params p)
     constexpr int kChunks = kBlockK * kUnits / kThreads;  // units per thread per tile
     constexpr int kDSteps = D / 16;                       // k-steps of the first product
     constexpr int kDBlocks = D / 32;                      // 32-row blocks of O^T
+    // fp16 row sums on the matrix cores (see weights() below); the 8-wave
+    // shapes have the registers for it, the smaller ones keep VALU dot2 sums
+    constexpr bool kSumOnMfma = std::is_same<T, _Float16>::value && NW == 8;
 
     // two stages of [group][K | V] tiles, as separate objects so the compiler
     // can tell copies into one stage from reads of the other
@@ -88,7 +91,9 @@ __global__ __launch_bounds__(64 * NW * SPLIT) void attn_fwd_kernel(Params p)
 
     const int tid = threadIdx.x;
     const int grp = SPLIT > 1 ? __builtin_amdgcn_readfirstlane(tid / 64 / NW) : 0;  // key-range group
-    const int wave = (tid / 64) % NW;                                // row block within the group
+    // wave-uniform (an SGPR): the row block and everything derived from it
+    // (its first and last rows, liveness, skip tests) stay out of VGPRs
+    const int wave = __builtin_amdgcn_readfirstlane((tid / 64) % NW);  // row block within the group
     const int lane = tid % 64;
     const int l32 = lane % 32;
     const int hi = lane / 32;
@@ -156,7 +161,14 @@ __global__ __launch_bounds__(64 * NW * SPLIT) void attn_fwd_kernel(Params p)
     for (int i = 0; i < kDBlocks; ++i) acc_o[i] = f32x16{};
     float m_run = -INFINITY;  // reference max of scale*log2(e)*s (log2 domain), -inf until a key is seen
     float neg_m = 0.f;        // -m_run, or 0 while m_run is -inf
-    float l_run = 0.f;        // sum of the rounded weights, this lane's half of the keys
+    // sum of the rounded weights: with kSumOnMfma the whole row's (every lane
+    // of the query holds it), otherwise this lane's half of the keys
+    float l_run = 0.f;
+    // A operand of the row-sum product (16x16x32): the word 0x3C003C00 (two
+    // fp16 ones) where row 4G of the selector picks the k-groups holding the
+    // query of lane group G, else zero (see weights())
+    const int sel_m = lane % 16, sel_g = lane / 16;
+    const uint32_t ones_word = (sel_m % 4 == 0 && (sel_g & 1) == ((sel_m >> 2) & 1)) ? 0x3C003C00u : 0u;
 
     // ---- global -> LDS copies of one K/V tile, straight into LDS (no VGPR
     // staging).  A wave-wide copy instruction writes 64 consecutive 16-byte
@@ -268,7 +280,9 @@ __global__ __launch_bounds__(64 * NW * SPLIT) void attn_fwd_kernel(Params p)
                     for (int e = 0; e < 8; ++e)
                         pf[e] = __builtin_amdgcn_exp2f(fmaf(s[ks / 2][8 * (ks % 2) + e], p.scale_log2, neg_m));
                     pv[ks] = __builtin_convertvector(pf, vec8);
-                    if constexpr (std::is_same<T, _Float16>::value) {
+                    if constexpr (kSumOnMfma) {
+                        (void)part;  // summed below on the matrix cores
+                    } else if constexpr (std::is_same<T, _Float16>::value) {
                         part[ks] = sum8(pv[ks], 0.f);  // the rounded weights, as the product uses them
                     } else {
                         // bf16 rounding of the weights (2^-8) would reach the lse of
@@ -282,9 +296,30 @@ __global__ __launch_bounds__(64 * NW * SPLIT) void attn_fwd_kernel(Params p)
                         asm volatile("" : "+v"(pv[ks]));
                     }
                 }
-                // fp16: four independent dot2 chains, combined pairwise (one chain
-                // of 16 dependent dot2 measured 4 % slower at the 128k shape)
-                if constexpr (std::is_same<T, _Float16>::value) l_tile = (part[0] + part[1]) + (part[2] + part[3]);
+                if constexpr (kSumOnMfma) {
+                    // Row sums of the rounded weights as a 16x16x32 product on the
+                    // matrix cores instead of 16 dot2 per lane: the B operand is
+                    // each 16-key slice of P^T as held for the second product
+                    // (lane 16g + n: query n + 16(g & 1), keys 8(g >> 1)..+7 of
+                    // the slice), the A operand a 0/1 selector whose row 4G sums
+                    // the k-groups g with g & 1 == G & 1.  Result row 4G, column n
+                    // sits in register 0 of lane 16G + n: that lane's own query,
+                    // summed over all 64 keys of the tile.  Products with 1 and 0
+                    // are exact and accumulate in fp32, as the dot2 sums did.  The
+                    // selector word is rebuilt per tile so that its four registers
+                    // are not live across the loop.
+                    uint32_t w = ones_word;
+                    asm volatile("" : "+v"(w));
+                    const f16x8 sel = __builtin_bit_cast(f16x8, u32x4{w, w, w, w});
+                    f32x4 ls = __builtin_amdgcn_mfma_f32_16x16x32_f16(sel, pv[0], f32x4{}, 0, 0, 0);
+#pragma unroll
+                    for (int ks = 1; ks < 4; ++ks) ls = __builtin_amdgcn_mfma_f32_16x16x32_f16(sel, pv[ks], ls, 0, 0, 0);
+                    l_tile = ls[0];
+                } else if constexpr (std::is_same<T, _Float16>::value) {
+                    // four independent dot2 chains, combined pairwise (one chain
+                    // of 16 dependent dot2 measured 4 % slower at the 128k shape)
+                    l_tile = (part[0] + part[1]) + (part[2] + part[3]);
+                }
             };
             weights();
             if (__any(!(l_tile <= kMaxTileSum) || m_run == -INFINITY)) {
@@ -383,7 +418,7 @@ __global__ __launch_bounds__(64 * NW * SPLIT) void attn_fwd_kernel(Params p)
 
     // ---- epilogue: one write of O and lse
     if (grp != 0 || !wave_live || qi >= L) return;
-    const float l_tot = half_swap_sum(l_run);
+    const float l_tot = kSumOnMfma ? l_run : half_swap_sum(l_run);
     const float inv = 1.f / l_tot;
     if (hi == 0) lseh[qi] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
     T *orow = oh + (int64_t)qi * D;

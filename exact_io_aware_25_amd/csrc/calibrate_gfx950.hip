@@ -8,6 +8,10 @@
 //         x of lane l%32 + 32;
 //       * buffer_load_dwordx4 ... lds: lane i's 16 bytes land at M0 + 16*i,
 //         read from lane i's own offset, and out-of-range lanes write zeros;
+//       * v_mfma_f32_16x16x32_f16 as the forward's row-sum product: with the
+//         0/1 selector as A and lane 16g + n holding 8 values as B, register 0
+//         of lane 16G + n is the sum of the 16 values of lanes 16g + n with
+//         g & 1 == G & 1 (the lanes of one query in the 32x32 layout);
 //       and reports (without failing) which SIMD each wave of an 8-wave
 //       workgroup runs on (HW_REG_HW_ID bits 5:4): --rates places its two
 //       wave roles on shared SIMDs by assuming waves w and w+4 share one.
@@ -101,6 +105,23 @@ __global__ void dma_layout(const unsigned *src, unsigned *out, int records)
     for (int i = lane; i < 1024; i += 64) out[i] = lds[i];
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// One wave: the forward's row-sum product on known B values.
+__global__ void rowsum_layout(float *out)
+{
+    const int lane = threadIdx.x;
+    const int m = lane % 16, g = lane / 16;
+    const _Float16 one = (m % 4 == 0 && (g & 1) == ((m >> 2) & 1)) ? (_Float16)1 : (_Float16)0;
+    f16x8 a, b;
+    for (int j = 0; j < 8; ++j) {
+        a[j] = one;
+        b[j] = (_Float16)((lane * 8 + j) % 61);
+    }
+    const f32x4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, f32x4{}, 0, 0, 0);
+    out[lane] = d[0];
+}
+
 static int run_checks()
 {
     int failures = 0;
@@ -155,6 +176,25 @@ static int run_checks()
         }
         std::printf("buffer_load ... lds placement (%d-byte range): %s\n", records,
                     failures > before ? "MISMATCH" : "ok");
+    }
+    {
+        const int before = failures;
+        float *d_f;
+        CHECK_HIP(hipMalloc(&d_f, 64 * sizeof(float)));
+        hipLaunchKernelGGL(rowsum_layout, dim3(1), dim3(64), 0, 0, d_f);
+        CHECK_HIP(hipDeviceSynchronize());
+        std::vector<float> hf(64);
+        CHECK_HIP(hipMemcpy(hf.data(), d_f, 64 * sizeof(float), hipMemcpyDeviceToHost));
+        CHECK_HIP(hipFree(d_f));
+        for (int lane = 0; lane < 64; ++lane) {
+            const int G = lane / 16, n = lane % 16;
+            int want = 0;
+            for (int g = 0; g < 4; ++g)
+                if ((g & 1) == (G & 1))
+                    for (int j = 0; j < 8; ++j) want += ((16 * g + n) * 8 + j) % 61;
+            if (hf[lane] != (float)want) ++failures;
+        }
+        std::printf("v_mfma_f32_16x16x32_f16 row-sum selector layout: %s\n", failures > before ? "MISMATCH" : "ok");
     }
     // wave placement (reported, not checked): 16 workgroups of 8 waves
     hipLaunchKernelGGL(simd_of_wave, dim3(16), dim3(512), 0, 0, d_i);

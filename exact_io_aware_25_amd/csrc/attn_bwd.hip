@@ -115,7 +115,7 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 12 / NW : 1) void attn_bwd_dkdv_
     __shared__ __attribute__((aligned(16))) char lds_b[kStageBytes];
 
     const int tid = threadIdx.x;
-    const int wave = tid / 64;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // wave-uniform: derived rows and tests stay in SGPRs
     const int lane = tid % 64;
     const int l32 = lane % 32;
     const int hi = lane / 32;
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(128 * NP) void attn_bwd_dkdv_pair_kernel(BwdParams 
     __shared__ __attribute__((aligned(16))) float xbuf[2][NP][16 * 64];  // P of a 32-query block, per pair
 
     const int tid = threadIdx.x;
-    const int wave = tid / 64;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // wave-uniform: derived rows and tests stay in SGPRs
     const int lane = tid % 64;
     const int l32 = lane % 32;
     const int hi = lane / 32;
@@ -589,7 +589,7 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_kernel(BwdParams p)
     __shared__ __attribute__((aligned(16))) char lds_b[2][kTileBytes];
 
     const int tid = threadIdx.x;
-    const int wave = tid / 64;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // wave-uniform: derived rows and tests stay in SGPRs
     const int lane = tid % 64;
     const int l32 = lane % 32;
     const int hi = lane / 32;

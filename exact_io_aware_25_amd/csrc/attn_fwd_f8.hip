@@ -104,7 +104,7 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_f8_kernel(F8Params p)
     __shared__ __attribute__((aligned(16))) char lds_b[2][kTileBytes];
 
     const int tid = threadIdx.x;
-    const int wave = tid / 64;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // wave-uniform: derived rows and tests stay in SGPRs
     const int lane = tid % 64;
     const int l32 = lane % 32;
     const int hi = lane / 32;

@@ -28,9 +28,10 @@ ATTN_ERR_SIZE = 7
 ATTN_ERR_FLAG = 8
 ATTN_ERR_SCALE = 9
 ATTN_ERR_ALIGN = 10
+ATTN_ERR_SCRATCH = 11
 
 EXPORTS = ("attn_fwd", "attn_fwd_bf16", "attn_fwd_fp8", "attn_bwd", "attn_bwd_bf16", "attn_bwd_workspace_size",
-           "attn_decode", "attn_decode_bf16", "attn_decode_workspace_size",
+           "attn_decode", "attn_decode_bf16", "attn_decode_workspace_size", "attn_decode_noalloc",
            "attn_launch_shape", "attn_status_string", "attn_resolve_scale")
 
 _lib = None
@@ -69,6 +70,9 @@ def library():
             fn = getattr(lib, name)
             fn.restype = ctypes.c_int
             fn.argtypes = dsig
+        fn = lib.attn_decode_noalloc
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int] * 10 + [ctypes.c_float, ctypes.c_void_p]
         lib.attn_decode_workspace_size.restype = ctypes.c_size_t
         lib.attn_decode_workspace_size.argtypes = [ctypes.c_int] * 6
         lib.attn_bwd_workspace_size.restype = ctypes.c_size_t
@@ -124,6 +128,15 @@ def attn_decode_bf16(q, k_cache, v_cache, block_table, seq_lens, out, lse, works
     return library().attn_decode_bf16(q, k_cache, v_cache, block_table, seq_lens, out, lse, workspace, B, H, H_kv,
                                       Lq, d, block_size, max_blocks_per_seq, num_blocks, max_seq_len, window, scale,
                                       stream)
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, block_table, seq_lens, out, lse, B, H, H_kv, Lq, d, block_size,
+                        max_blocks_per_seq, num_blocks, max_seq_len, window, scale, stream) -> int:
+    """fp16 decode into the library's static scratch (no workspace argument,
+    nothing allocated); pointers are integer device addresses."""
+    return library().attn_decode_noalloc(q, k_cache, v_cache, block_table, seq_lens, out, lse, B, H, H_kv, Lq, d,
+                                         block_size, max_blocks_per_seq, num_blocks, max_seq_len, window, scale,
+                                         stream)
 
 
 def attn_decode_workspace_size(B, H, H_kv, Lq, d, max_seq_len) -> int:
@@ -231,7 +244,7 @@ def _int32(**values):
 def _check(status):
     if status != ATTN_OK:
         msg = attn_status_string(status)
-        if status in (1, 2, 3, 4, 5, 8, 9, 10):
+        if status in (1, 2, 3, 4, 5, 8, 9, 10, 11):
             raise ValueError(msg)
         raise AttnError(status, msg)
 

@@ -28,6 +28,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "attn.h"
 #include "attn_common.h"
@@ -45,6 +46,7 @@ struct DecParams {
     float *lse;
     float *part;        // [rows_total][n_chunks][D] unnormalised O, then [rows_total][n_chunks][2] (m, l)
     int B, H, H_kv, Lq, group, rows;  // rows = group * Lq: query rows per K/V head
+    int d;                            // head size (host side: picks the kernel instance)
     int bs, bs_shift, max_blocks, num_blocks, max_len, window;
     int chunk, n_chunks, n_rowblk, n_cgroups;
     float scale_log2;
@@ -384,12 +386,17 @@ hipError_t launch_decode(DecParams p, hipStream_t stream)
                            dim3((unsigned)rows_total), dim3(256), kargs, 0, stream);
 }
 
+// Checks every argument but the workspace and fills the launch parameters
+// (all but p->part); *bytes_ws receives the workspace the call needs.  Makes
+// no HIP call.  ATTN_OK with p->B == 0 is an empty problem.
 template <typename T>
-int attn_decode_impl(const void *q, const void *k_cache, const void *v_cache, const int *block_table,
-                     const int *seq_lens, void *out, float *lse, void *workspace, int B, int H, int H_kv, int Lq,
-                     int d, int block_size, int max_blocks, int num_blocks, int max_seq_len, int window,
-                     float scale, void *stream)
+int decode_plan(const void *q, const void *k_cache, const void *v_cache, const int *block_table,
+                const int *seq_lens, void *out, float *lse, int B, int H, int H_kv, int Lq, int d, int block_size,
+                int max_blocks, int num_blocks, int max_seq_len, int window, float scale, DecParams *pp,
+                size_t *bytes_ws_out)
 {
+    DecParams &p = *pp;
+    p.B = 0;
     if (B < 0 || H < 1 || H_kv < 1 || H % H_kv != 0 || Lq < 1 || max_blocks < 1 || num_blocks < 1 ||
         max_seq_len < 1)
         return ATTN_ERR_SHAPE;
@@ -400,11 +407,10 @@ int attn_decode_impl(const void *q, const void *k_cache, const void *v_cache, co
     if (window < -1) return ATTN_ERR_WINDOW;
     if (std::isinf(scale)) return ATTN_ERR_SCALE;
     if (B == 0) return ATTN_OK;
-    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out || !lse || !workspace)
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out || !lse)
         return ATTN_ERR_NULL;
     const uintptr_t a16 = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
-                          reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(out) |
-                          reinterpret_cast<uintptr_t>(workspace);
+                          reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(out);
     const uintptr_t a4 = reinterpret_cast<uintptr_t>(lse) | reinterpret_cast<uintptr_t>(block_table) |
                          reinterpret_cast<uintptr_t>(seq_lens);
     if ((a16 & 15) || (a4 & 3)) return ATTN_ERR_ALIGN;
@@ -426,19 +432,18 @@ int attn_decode_impl(const void *q, const void *k_cache, const void *v_cache, co
     const size_t bytes_table = (size_t)B * max_blocks * sizeof(int);
     const size_t bytes_lens = (size_t)B * sizeof(int);
     const size_t bytes_lse = (size_t)B * H * Lq * sizeof(float);
-    const size_t bytes_ws = decode_workspace_bytes(B, H, H_kv, Lq, d, max_seq_len);
     const void *ins[] = {q, k_cache, v_cache, block_table, seq_lens};
     const size_t in_bytes[] = {bytes_q, bytes_cache, bytes_cache, bytes_table, bytes_lens};
-    const void *outs[] = {out, lse, workspace};
-    const size_t out_bytes[] = {bytes_q, bytes_lse, bytes_ws};
-    for (int i = 0; i < 3; ++i) {
+    const void *outs[] = {out, lse};
+    const size_t out_bytes[] = {bytes_q, bytes_lse};
+    for (int i = 0; i < 2; ++i) {
         for (int j = 0; j < 5; ++j)
             if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return ATTN_ERR_ALIAS;
-        for (int j = i + 1; j < 3; ++j)
+        for (int j = i + 1; j < 2; ++j)
             if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return ATTN_ERR_ALIAS;
     }
+    *bytes_ws_out = decode_workspace_bytes(B, H, H_kv, Lq, d, max_seq_len);
 
-    DecParams p;
     p.q = q;
     p.kc = k_cache;
     p.vc = v_cache;
@@ -446,7 +451,7 @@ int attn_decode_impl(const void *q, const void *k_cache, const void *v_cache, co
     p.lens = seq_lens;
     p.o = out;
     p.lse = lse;
-    p.part = static_cast<float *>(workspace);
+    p.part = nullptr;
     p.B = B;
     p.H = H;
     p.H_kv = H_kv;
@@ -464,15 +469,97 @@ int attn_decode_impl(const void *q, const void *k_cache, const void *v_cache, co
     p.n_rowblk = n_rowblk;
     p.n_cgroups = n_cgroups;
     p.scale_log2 = attn_resolve_scale(scale, d) * 1.4426950408889634f;
+    p.d = d;
+    return ATTN_OK;
+}
 
+template <typename T>
+int decode_launch(const DecParams &p, void *stream)
+{
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const hipError_t err = d == 64 ? launch_decode<T, 64>(p, s) : launch_decode<T, 128>(p, s);
+    const hipError_t err = p.d == 64 ? launch_decode<T, 64>(p, s) : launch_decode<T, 128>(p, s);
     return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+template <typename T>
+int attn_decode_impl(const void *q, const void *k_cache, const void *v_cache, const int *block_table,
+                     const int *seq_lens, void *out, float *lse, void *workspace, int B, int H, int H_kv, int Lq,
+                     int d, int block_size, int max_blocks, int num_blocks, int max_seq_len, int window,
+                     float scale, void *stream)
+{
+    DecParams p;
+    size_t bytes_ws = 0;
+    const int st = decode_plan<T>(q, k_cache, v_cache, block_table, seq_lens, out, lse, B, H, H_kv, Lq, d,
+                                  block_size, max_blocks, num_blocks, max_seq_len, window, scale, &p, &bytes_ws);
+    if (st != ATTN_OK || p.B == 0) return st;
+    if (!workspace) return ATTN_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(workspace) & 15) return ATTN_ERR_ALIGN;
+    const size_t bytes_q = (size_t)B * H * Lq * d * sizeof(T);
+    const size_t bytes_cache = (size_t)num_blocks * H_kv * block_size * d * sizeof(T);
+    const void *others[] = {q, k_cache, v_cache, block_table, seq_lens, out, lse};
+    const size_t other_bytes[] = {bytes_q, bytes_cache, bytes_cache, (size_t)B * max_blocks * sizeof(int),
+                                  (size_t)B * sizeof(int), bytes_q, (size_t)B * H * Lq * sizeof(float)};
+    for (int j = 0; j < 7; ++j)
+        if (overlaps(workspace, bytes_ws, others[j], other_bytes[j])) return ATTN_ERR_ALIAS;
+    p.part = static_cast<float *>(workspace);
+    return decode_launch<T>(p, stream);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- allocation-free entry point
+// The partial results of attn_decode_noalloc live in this array, one copy per
+// device (the runtime loads it with the code object and keeps it until the
+// process ends).  In host code `scratch` is only a stand-in for the device
+// symbol: the device address comes from hipGetSymbolAddress, once per device,
+// and only that address is ever handed to a kernel.
+static constexpr size_t kDecodeScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once looked up
+
+// The current device's copy of `scratch` (looked up on the first call made
+// with that device current).
+int scratch_pointer(void **ptr)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ATTN_ERR_LAUNCH;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return ATTN_OK;
 }
 
 }  // namespace
 
 extern "C" {
+
+int attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache, const int *block_table,
+                        const int *seq_lens, void *out, float *lse, int B, int H, int H_kv, int Lq, int d,
+                        int block_size, int max_blocks_per_seq, int num_blocks, int max_seq_len, int window,
+                        float scale, void *stream)
+{
+    DecParams p;
+    size_t bytes_ws = 0;
+    const int st = decode_plan<_Float16>(q, k_cache, v_cache, block_table, seq_lens, out, lse, B, H, H_kv, Lq, d,
+                                         block_size, max_blocks_per_seq, num_blocks, max_seq_len, window, scale, &p,
+                                         &bytes_ws);
+    if (st != ATTN_OK || p.B == 0) return st;
+    if (bytes_ws > kDecodeScratchBytes) return ATTN_ERR_SCRATCH;
+    void *ws = nullptr;
+    const int sp = scratch_pointer(&ws);
+    if (sp != ATTN_OK) return sp;
+    p.part = static_cast<float *>(ws);
+    return decode_launch<_Float16>(p, stream);
+}
 
 size_t attn_decode_workspace_size(int B, int H, int H_kv, int Lq, int d, int max_seq_len)
 {

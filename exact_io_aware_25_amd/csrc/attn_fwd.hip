@@ -611,6 +611,7 @@ const char *attn_status_string(int status)
     case ATTN_ERR_FLAG: return "causal must be 0 or 1";
     case ATTN_ERR_SCALE: return "scale must be finite";
     case ATTN_ERR_ALIGN: return "tensors must be 16-byte aligned (lse 4-byte aligned)";
+    case ATTN_ERR_SCRATCH: return "the call needs more workspace than the static scratch of attn_decode_noalloc holds";
     default: return "unknown status";
     }
 }

@@ -75,7 +75,9 @@ enum attn_status {
     ATTN_ERR_SIZE = 7,     /* a tensor or the grid is too large to index                    */
     ATTN_ERR_FLAG = 8,     /* causal is neither 0 nor 1                                     */
     ATTN_ERR_SCALE = 9,    /* scale is +/- infinity                                         */
-    ATTN_ERR_ALIGN = 10    /* a tensor not 16-byte aligned, or lse not 4-byte aligned        */
+    ATTN_ERR_ALIGN = 10,   /* a tensor not 16-byte aligned, or lse not 4-byte aligned        */
+    ATTN_ERR_SCRATCH = 11  /* attn_decode_noalloc: the call needs more workspace than its
+                              static scratch holds (64 MiB)                                 */
 };
 
 /*
@@ -205,6 +207,26 @@ int attn_decode_bf16(const void *q, const void *k_cache, const void *v_cache, co
 /* Bytes of workspace attn_decode / attn_decode_bf16 need; 0 for invalid
  * arguments.  Host-only. */
 size_t attn_decode_workspace_size(int B, int H, int H_kv, int Lq, int d, int max_seq_len);
+
+/* attn_decode (fp16) for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The same arguments as attn_decode without `workspace`: the
+ * per-chunk partial results go to a static device array of 64 MiB
+ * (67108864 bytes) that the library holds
+ * on every device it runs on until the process ends; the call allocates
+ * nothing.  A call whose attn_decode_workspace_size(...) exceeds it returns
+ * ATTN_ERR_SCRATCH before any HIP call.  The first call on a device looks up
+ * that device's copy of the array (the device current at the call, which
+ * must be the stream's device).  Every call on one device shares the array,
+ * so calls that overlap on one device (other streams, other threads) race;
+ * calls on one stream are ordered and safe.  Its contents are undefined
+ * between calls (nothing in it needs to start at zero).  Other behaviour and
+ * every argument check as for attn_decode. */
+int attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache, const int *block_table,
+                        const int *seq_lens, void *out, float *lse,
+                        int B, int H, int H_kv, int Lq, int d, int block_size, int max_blocks_per_seq,
+                        int num_blocks, int max_seq_len, int window, float scale, void *stream);
+
 
 /* The fp32 scale the kernels use for a given scale argument and head size:
  * `scale` itself when finite and > 0, else the fp32 value nearest 1/sqrt(d).

@@ -246,3 +246,35 @@ def test_binding_refuses_explicit_bad_scale():
             attn.forward(q, q, q, scale=bad)
         with pytest.raises(ValueError, match="scale"):
             attn.backward(q, q, q, q, torch.zeros(1, 1, 4), q, scale=bad)
+
+
+def call_noalloc(q=DQ_, kc=KC, vc=VC, bt=BT, sl=SL, o=DO_, lse=DL, B=2, H=8, H_kv=2, Lq=1, d=128, bs=16,
+                 max_blocks=64, num_blocks=128, max_len=1024, window=-1, scale=0.0):
+    return attn.attn_decode_noalloc(q, kc, vc, bt, sl, o, lse, B, H, H_kv, Lq, d, bs, max_blocks, num_blocks,
+                                    max_len, window, scale, None)
+
+
+def test_decode_noalloc_argument_errors():
+    """The allocation-free decode entry point checks its arguments as
+    attn_decode does, and refuses a call whose workspace would exceed its
+    64 MiB static scratch, all before any HIP call."""
+    for name in ("q", "kc", "vc", "bt", "sl", "o", "lse"):
+        assert call_noalloc(**{name: 0}) == attn.ATTN_ERR_NULL, name
+    assert call_noalloc(H=7) == attn.ATTN_ERR_SHAPE
+    assert call_noalloc(bs=24) == attn.ATTN_ERR_SHAPE
+    assert call_noalloc(d=96) == attn.ATTN_ERR_HEAD_DIM
+    assert call_noalloc(window=-2) == attn.ATTN_ERR_WINDOW
+    assert call_noalloc(scale=float("inf")) == attn.ATTN_ERR_SCALE
+    assert call_noalloc(o=DQ_) == attn.ATTN_ERR_ALIAS
+    assert call_noalloc(q=DQ_ + 8) == attn.ATTN_ERR_ALIGN
+    assert call_noalloc(q=0, kc=0, vc=0, bt=0, sl=0, o=0, lse=0, B=0) == attn.ATTN_OK
+    # 8 query rows per K/V head over 128k-token sequences need 130 MiB of
+    # partial results; 16 MiB for one new token each
+    limit = 64 << 20
+    big = dict(B=64, H=32, H_kv=8, Lq=8, d=128, bs=16, max_blocks=8192, num_blocks=8192, max_len=131072)
+    assert attn.attn_decode_workspace_size(64, 32, 8, 8, 128, 131072) > limit
+    far = dict(zip(("q", "kc", "vc", "bt", "sl", "o", "lse"), (i << 40 for i in range(1, 8))))  # no overlaps
+    assert call_noalloc(**big, **far) == attn.ATTN_ERR_SCRATCH
+    assert call_noalloc(**dict(big, Lq=1), **dict(far, q=0)) == attn.ATTN_ERR_NULL  # checks still come first
+    assert attn.attn_decode_workspace_size(8, 32, 8, 1, 128, 131072) < limit
+    assert "scratch" in attn.attn_status_string(attn.ATTN_ERR_SCRATCH)

@@ -166,28 +166,17 @@ __global__ __launch_bounds__(64 * NW, D == 64 ? 12 / NW : 1) void attn_bwd_dkdv_
     }
 
     // ---- per-lane LDS byte offsets
-    const int qrow = k_row_for_lane(l32);
     int roff[kDSteps];  // A operand rows (queries) of S = Q K^T and dP = dO V^T
 #pragma unroll
-    for (int ds = 0; ds < kDSteps; ++ds)
-        roff[ds] = qrow * kRowBytes + 16 * ((2 * ds + hi) ^ dual_swizzle<D>(qrow));
-    const int tr_row = 8 * hi + ((lane >> 2) & 3);
-    const int tr_unit = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    for (int ds = 0; ds < kDSteps; ++ds) roff[ds] = k_frag_offset<D, kSwzDual>(lane, ds);
     int troff[kDBlocks][2];  // transposing reads of dO^T and Q^T (rows +0 and +4)
 #pragma unroll
     for (int db = 0; db < kDBlocks; ++db)
 #pragma unroll
-        for (int r4 = 0; r4 < 2; ++r4) {
-            const int row = tr_row + 4 * r4;
-            troff[db][r4] = row * kRowBytes + 16 * ((4 * db + tr_unit) ^ dual_swizzle<D>(row)) + 8 * (lane & 1);
-        }
+        for (int r4 = 0; r4 < 2; ++r4) troff[db][r4] = v_tr_offset<D, kSwzDual>(lane, db, r4);
     int ld_off[kChunks];  // source offsets of the tile copies (swizzled placement)
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-        const int unit_idx = (c * NW + wave) * 64 + lane;
-        const int row = unit_idx / kUnits, phys = unit_idx % kUnits;
-        ld_off[c] = row * kRowBytes + 16 * (phys ^ dual_swizzle<D>(row));
-    }
+    for (int c = 0; c < kChunks; ++c) ld_off[c] = copy_src_offset<D, kSwzDual>((c * NW + wave) * 64 + lane);
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
     // ---- global -> LDS copy of step n: the Q and dO tiles of (head, query
@@ -401,28 +390,17 @@ __global__ __launch_bounds__(128 * NP) void attn_bwd_dkdv_pair_kernel(BwdParams 
     for (int i = 0; i < kDBlocks; ++i) acc[i] = f32x16{};
 
     // ---- per-lane LDS byte offsets (as in the single-wave kernel)
-    const int qrow = k_row_for_lane(l32);
     int roff[kDSteps];
 #pragma unroll
-    for (int ds = 0; ds < kDSteps; ++ds)
-        roff[ds] = qrow * kRowBytes + 16 * ((2 * ds + hi) ^ dual_swizzle<D>(qrow));
-    const int tr_row = 8 * hi + ((lane >> 2) & 3);
-    const int tr_unit = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    for (int ds = 0; ds < kDSteps; ++ds) roff[ds] = k_frag_offset<D, kSwzDual>(lane, ds);
     int troff[kDBlocks][2];
 #pragma unroll
     for (int db = 0; db < kDBlocks; ++db)
 #pragma unroll
-        for (int r4 = 0; r4 < 2; ++r4) {
-            const int row = tr_row + 4 * r4;
-            troff[db][r4] = row * kRowBytes + 16 * ((4 * db + tr_unit) ^ dual_swizzle<D>(row)) + 8 * (lane & 1);
-        }
+        for (int r4 = 0; r4 < 2; ++r4) troff[db][r4] = v_tr_offset<D, kSwzDual>(lane, db, r4);
     int ld_off[kChunks];
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-        const int unit_idx = (c * NW + wave) * 64 + lane;
-        const int row = unit_idx / kUnits, phys = unit_idx % kUnits;
-        ld_off[c] = row * kRowBytes + 16 * (phys ^ dual_swizzle<D>(row));
-    }
+    for (int c = 0; c < kChunks; ++c) ld_off[c] = copy_src_offset<D, kSwzDual>((c * NW + wave) * 64 + lane);
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
     auto copy_step = [&](int n, char *stage) {
@@ -644,31 +622,24 @@ __global__ __launch_bounds__(64 * NW) void attn_bwd_dq_kernel(BwdParams p)
 
     // ---- per-lane LDS byte offsets: K is read both by rows and transposed
     // (dual swizzle), V only by rows (K swizzle)
-    const int krow = k_row_for_lane(l32);
     int koff[kDSteps], voff[kDSteps];
 #pragma unroll
     for (int ds = 0; ds < kDSteps; ++ds) {
-        koff[ds] = krow * kRowBytes + 16 * ((2 * ds + hi) ^ dual_swizzle<D>(krow));
-        voff[ds] = krow * kRowBytes + 16 * ((2 * ds + hi) ^ k_swizzle<D>(krow));
+        koff[ds] = k_frag_offset<D, kSwzDual>(lane, ds);
+        voff[ds] = k_frag_offset<D, kSwzK>(lane, ds);
     }
-    const int tr_row = 8 * hi + ((lane >> 2) & 3);
-    const int tr_unit = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
     int ktr[kDBlocks][2];
 #pragma unroll
     for (int db = 0; db < kDBlocks; ++db)
 #pragma unroll
-        for (int r4 = 0; r4 < 2; ++r4) {
-            const int row = tr_row + 4 * r4;
-            ktr[db][r4] = row * kRowBytes + 16 * ((4 * db + tr_unit) ^ dual_swizzle<D>(row)) + 8 * (lane & 1);
-        }
+        for (int r4 = 0; r4 < 2; ++r4) ktr[db][r4] = v_tr_offset<D, kSwzDual>(lane, db, r4);
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     int ld_k[kChunks], ld_v[kChunks];
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
         const int unit_idx = (c * NW + wave) * 64 + lane;
-        const int row = unit_idx / kUnits, phys = unit_idx % kUnits;
-        ld_k[c] = row * kRowBytes + 16 * (phys ^ dual_swizzle<D>(row));
-        ld_v[c] = row * kRowBytes + 16 * (phys ^ k_swizzle<D>(row));
+        ld_k[c] = copy_src_offset<D, kSwzDual>(unit_idx);
+        ld_v[c] = copy_src_offset<D, kSwzK>(unit_idx);
     }
     auto copy_tile = [&](int t, char (*stage)[kTileBytes]) {
         const int j0 = t * kBlockK;

@@ -125,19 +125,12 @@ __global__ __launch_bounds__(64 * kDecWaves) void attn_decode_partial_kernel(Dec
     const int krow = k_row_for_lane(l32);  // A-operand row order (bits 2 and 3 swapped)
 
     // transposing-read offsets of the V tile (rows 8hi + a and +4, as in the forward)
-    const int tr_row = 8 * hi + ((lane >> 2) & 3);
-    const int tr_unit = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
     int voff[kDBlocks];
 #pragma unroll
-    for (int db = 0; db < kDBlocks; ++db)
-        voff[db] = tr_row * kRowBytes + 16 * ((4 * db + tr_unit) ^ v_swizzle<D>(tr_row)) + 8 * (lane & 1);
+    for (int db = 0; db < kDBlocks; ++db) voff[db] = v_tr_offset<D, kSwzV>(lane, db);
     int ld_v[kHalfCopies];  // source offsets within a 16-row half tile (swizzled placement)
 #pragma unroll
-    for (int cc = 0; cc < kHalfCopies; ++cc) {
-        const int unit = cc * 64 + lane;
-        const int row = unit / kUnits, phys = unit % kUnits;
-        ld_v[cc] = row * kRowBytes + 16 * (phys ^ v_swizzle<D>(row));
-    }
+    for (int cc = 0; cc < kHalfCopies; ++cc) ld_v[cc] = copy_src_offset<D, kSwzV>(cc * 64 + lane);
 
     // The physical blocks of the two 16-key halves of tile t (wave-uniform).
     // They are fetched two tiles ahead, so a tile's data loads never wait on

@@ -76,8 +76,7 @@ __global__ __launch_bounds__(64 * NW * SPLIT) void attn_fwd_kernel(Params p)
     constexpr int kBlockQ = kRowsPerWave * NW;  // query rows per workgroup
     constexpr int kRowBytes = 2 * D;                      // one K or V row in LDS
     constexpr int kTileBytes = kBlockK * kRowBytes;       // one K or V tile
-    constexpr int kUnits = D / 8;                         // 16-byte units per row
-    constexpr int kChunks = kBlockK * kUnits / kThreads;  // units per thread per tile
+    constexpr int kChunks = kBlockK * (D / 8) / kThreads;  // 16-byte units per thread per tile
     constexpr int kDSteps = D / 16;                       // k-steps of the first product
     constexpr int kDBlocks = D / 32;                      // 32-row blocks of O^T
     // fp16 row sums on the matrix cores (see weights() below); the 8-wave
@@ -117,16 +116,10 @@ __global__ __launch_bounds__(64 * NW * SPLIT) void attn_fwd_kernel(Params p)
     // ---- key range of the workgroup, and the tiles that cover it
     const int q_first = qblk * kBlockQ;
     const int q_last = min(L, q_first + kBlockQ) - 1;
-    int kv_begin = 0, kv_end = L;
-    if (WINDOW) kv_begin = max(0, q_first - p.window);
-    if (CAUSAL) kv_end = q_last + 1;
-    else if (WINDOW) kv_end = min(L, q_last + p.window + 1);
-    const int t_first = kv_begin / kBlockK;
-    const int t_last = (kv_end + kBlockK - 1) / kBlockK;  // one past
-    const int chunk = SPLIT > 1 ? (t_last - t_first + SPLIT - 1) / SPLIT : t_last - t_first;
-    const int t_begin = SPLIT > 1 ? t_first + grp * chunk : t_first;  // this group's tiles
-    const int t_end = SPLIT > 1 ? min(t_last, t_begin + chunk) : t_last;
-    const int t_stop = SPLIT > 1 ? t_begin + chunk : t_last;          // steps every group runs
+    const TileRange tiles = key_tiles<CAUSAL, WINDOW, SPLIT>(q_first, q_last, L, p.window, kBlockK, grp);
+    const int t_begin = tiles.t_begin;  // this group's tiles
+    const int t_end = tiles.t_end;
+    const int t_stop = tiles.t_stop;    // steps every group runs
 
     // ---- this wave's query rows
     const int qa = q_first + wave * kRowsPerWave;
@@ -145,17 +138,12 @@ __global__ __launch_bounds__(64 * NW * SPLIT) void attn_fwd_kernel(Params p)
     }
 
     // ---- per-lane LDS byte offsets (swizzled), fixed for the whole pass
-    const int krow = k_row_for_lane(l32);
     int koff[kDSteps];
 #pragma unroll
-    for (int ds = 0; ds < kDSteps; ++ds)
-        koff[ds] = krow * kRowBytes + 16 * ((2 * ds + hi) ^ k_swizzle<D>(krow));
-    const int tr_row = 8 * (lane >> 5) + ((lane >> 2) & 3);  // + 16*ks + 4*r
-    const int tr_unit = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-    int voff[kDBlocks];
+    for (int ds = 0; ds < kDSteps; ++ds) koff[ds] = k_frag_offset<D, kSwzK>(lane, ds);
+    int voff[kDBlocks];  // + 16 ks rows per key slice, + 4 rows for the second read
 #pragma unroll
-    for (int db = 0; db < kDBlocks; ++db)
-        voff[db] = tr_row * kRowBytes + 16 * ((4 * db + tr_unit) ^ v_swizzle<D>(tr_row)) + 8 * (lane & 1);
+    for (int db = 0; db < kDBlocks; ++db) voff[db] = v_tr_offset<D, kSwzV>(lane, db);
     f32x16 acc_o[kDBlocks];
 #pragma unroll
     for (int i = 0; i < kDBlocks; ++i) acc_o[i] = f32x16{};
@@ -181,9 +169,8 @@ __global__ __launch_bounds__(64 * NW * SPLIT) void attn_fwd_kernel(Params p)
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
         const int unit_idx = (c * kWaves + wave) * 64 + lane;  // LDS unit this lane fills
-        const int row = unit_idx / kUnits, phys = unit_idx % kUnits;
-        ld_k[c] = row * kRowBytes + 16 * (phys ^ k_swizzle<D>(row));
-        ld_v[c] = row * kRowBytes + 16 * (phys ^ v_swizzle<D>(row));
+        ld_k[c] = copy_src_offset<D, kSwzK>(unit_idx);
+        ld_v[c] = copy_src_offset<D, kSwzV>(unit_idx);
     }
     auto copy_tile = [&](int t, char (*stage)[2][kTileBytes]) {
         const int j0 = t * kBlockK;
@@ -213,20 +200,10 @@ __global__ __launch_bounds__(64 * NW * SPLIT) void attn_fwd_kernel(Params p)
         if (t + 1 < t_end) copy_tile(t + 1, nxt);
 
         const int j0 = t * kBlockK;
-        const int j_last = j0 + kBlockK - 1;
-        bool skip = !wave_live || (SPLIT > 1 && t >= t_end);
-        if (CAUSAL) skip = skip || j0 > qb;
-        if (WINDOW) {
-            skip = skip || j_last < qa - p.window;
-            if (!CAUSAL) skip = skip || j0 > qb + p.window;
-        }
+        const int cls = tile_class<CAUSAL, WINDOW>(j0, qa, qb, L, p.window, kBlockK);
+        const bool skip = !wave_live || (SPLIT > 1 && t >= t_end) || cls == 0;
         if (!skip) {
-            bool full = j_last < L;
-            if (CAUSAL) full = full && j_last <= qa;
-            if (WINDOW) {
-                full = full && j0 >= qb - p.window;
-                if (!CAUSAL) full = full && j_last <= qa + p.window;
-            }
+            const bool full = cls == 1;
 
             // S^T for the two 32-key blocks of the tile
             const char *tk = cur[grp][0];
@@ -378,17 +355,17 @@ __global__ __launch_bounds__(64 * NW * SPLIT) void attn_fwd_kernel(Params p)
     // round, through the now idle stage buffers: with M = max(m_0, m_s),
     // O = 2^(m_0-M) O_0 + 2^(m_s-M) O_s and likewise the sums
     if constexpr (SPLIT > 1) {
-        constexpr int kPart = 16 * kDBlocks + 2;  // floats per lane: O^T, reference max, sum
-        constexpr int kSlotBytes = 64 * kPart * 4;
-        constexpr int kPerBuffer = (int)sizeof(lds_a) / kSlotBytes;  // wave slots per stage buffer
-        constexpr int kBatch = 2 * kPerBuffer < NW ? 2 * kPerBuffer : NW;  // row blocks merged per round
-        static_assert(kPerBuffer >= 1, "merge slot does not fit");
+        typedef MergeLayout<D, NW, SPLIT> ML;
+        constexpr int kPart = ML::kPart;  // floats per lane: O^T, reference max, sum
+        constexpr int kPerBuffer = ML::kPerBuffer;  // wave slots per stage buffer
+        constexpr int kBatch = ML::kBatch;          // row blocks merged per round
+        static_assert(ML::kBufferBytes == (int)sizeof(lds_a) && kPerBuffer >= 1, "merge slot does not fit");
         for (int s = 1; s < SPLIT; ++s) {
             for (int first = 0; first < NW; first += kBatch) {
                 const int i = wave - first;  // slot of this wave in the round
                 const bool in_round = i >= 0 && i < kBatch;
                 float *slot = reinterpret_cast<float *>(i < kPerBuffer ? &lds_a[0][0][0] : &lds_b[0][0][0]) +
-                              (i % kPerBuffer) * 64 * kPart;
+                              ML::slot_float_offset(i);
                 __syncthreads();  // the previous round (or the last tile) is done with the buffers
                 if (grp == s && in_round) {
 #pragma unroll

@@ -75,18 +75,6 @@ __device__ __forceinline__ int pack4_f8(float a, float b, float c, float d)
     return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, x, true);
 }
 
-// XOR swizzle of the 16-byte units of an fp8 tile row (D/16 units per row),
-// found by exhaustive search over linear functions of the row bits so that
-// both reads are free of bank conflicts (32- and 64-bank models): the K rows
-// read 16 bytes per lane from rows k_row_for_lane(0..31), the V rows read by
-// the 8-bit transposing load, 8 rows x 16 bytes per 16-lane group.
-template <int D> __device__ __forceinline__ int f8_swizzle(int row)
-{
-    const int b0 = row & 1, b1 = (row >> 1) & 1, b2 = (row >> 2) & 1, b3 = (row >> 3) & 1;
-    if (D == 64) return (b1 ^ b2) | ((b2 ^ b3) << 1);
-    return b1 | ((b0 ^ b2) << 1) | ((b0 ^ b1 ^ b3) << 2);
-}
-
 template <int D, bool CAUSAL, bool WINDOW, int NW>
 __global__ __launch_bounds__(64 * NW) void attn_fwd_f8_kernel(F8Params p)
 {
@@ -153,21 +141,14 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_f8_kernel(F8Params p)
 
     // LDS offsets (swizzled): K rows for the A operand, two 16-byte units per
     // 64-deep step; V rows for the transposing reads
-    const int krow = k_row_for_lane(l32);
     int koff[kDSteps][2];
 #pragma unroll
     for (int ds = 0; ds < kDSteps; ++ds)
 #pragma unroll
-        for (int sp = 0; sp < 2; ++sp)
-            koff[ds][sp] = krow * kRowBytes + 16 * ((4 * ds + 2 * hi + sp) ^ f8_swizzle<D>(krow));
-    const int grp = lane / 16, li = lane % 16;
-    // read rho = 2kb + t addresses key row 32kb + 16t + 8*(grp/2) + li/2 at
-    // d bytes 32db + 16*(grp%2) + 8*(li%2)
-    const int vrow = 8 * (grp / 2) + li / 2;
+        for (int sp = 0; sp < 2; ++sp) koff[ds][sp] = f8_k_frag_offset<D>(lane, ds, sp);
     int voff[kDBlocks];
 #pragma unroll
-    for (int db = 0; db < kDBlocks; ++db)
-        voff[db] = vrow * kRowBytes + 16 * ((2 * db + grp % 2) ^ f8_swizzle<D>(vrow)) + 8 * (li % 2);
+    for (int db = 0; db < kDBlocks; ++db) voff[db] = f8_v_tr_offset<D>(lane, db);
 
     f32x16 acc_o[kDBlocks];
 #pragma unroll
@@ -180,10 +161,7 @@ __global__ __launch_bounds__(64 * NW) void attn_fwd_f8_kernel(F8Params p)
     int ld_off[kChunks];
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
-        const int unit = (c * NW + wave) * 64 + lane;                 // 0 .. kUnits-1
-        const int u = unit % (kTileBytes / 16);
-        const int row = u / (D / 16), phys = u % (D / 16);
-        ld_off[c] = row * kRowBytes + 16 * (phys ^ f8_swizzle<D>(row));  // the unit the swizzle puts here
+        ld_off[c] = f8_copy_src_offset<D>((c * NW + wave) * 64 + lane);  // the unit the swizzle puts here
     }
     auto copy_tile = [&](int t, char (*stage)[kTileBytes]) {
         const int j0 = t * kBlockK;

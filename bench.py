@@ -416,6 +416,52 @@ def roofline_block(w, ms):
             "traffic": profiled_traffic(w, "attn_fwd", source)}
 
 
+ORACLE_TIMING_WORKLOADS = ("p2_accuracy", "causal_4k", "noncausal_2k_f16", "noncausal_2k_bf16", "causal_8k",
+                           "causal_16k", "causal_32k", "swa_gqa_16k")
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_timings(steps: int):
+    """The whole fp64 oracle (every row) on the host cores for the workloads
+    whose oracle finishes in seconds to a minute, beside the GPU's median and
+    minimum launch time of the same workload and the parity of every output
+    element; one JSON line per workload, to stderr."""
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        threads = min(threads, int(os.environ["OMP_NUM_THREADS"]))
+    model = cpu_model()
+    for name in ORACLE_TIMING_WORKLOADS:
+        w = WORKLOADS[name]
+        r = time_workload(w, steps, 5)
+        q, k, v = (t.cpu() for t in r["inputs"])
+        t0 = time.perf_counter()
+        ref_o, ref_l = oracle.attention(q, k, v, w.dtype, w.causal, w.window, w.scale, threads=threads)
+        cpu_s = time.perf_counter() - t0
+        err_o = np.abs(r["out"].double().cpu().numpy() - ref_o)
+        err_l = np.abs(r["lse"].double().cpu().numpy() - ref_l)
+        flops = algorithmic_flops(w)
+        print(json.dumps({"oracle_timing": name, "dtype": w.dtype, "B": w.B, "H": w.H, "H_kv": w.H_kv, "L": w.L,
+                          "d": w.d, "causal": w.causal, "window": w.window,
+                          "oracle_s": round(cpu_s, 3), "oracle_tflops": flops / cpu_s / 1e12,
+                          "cores": threads, "cpu_model": model,
+                          "gpu_ms_mean": round(r["ms"], 5), "gpu_ms_median": round(r["ms_median"], 5),
+                          "gpu_ms_min": round(r["ms_min"], 5), "gpu_over_oracle": round(cpu_s / (r["ms"] * 1e-3), 1),
+                          "max_abs_o": float(err_o.max()), "mean_abs_o": float(err_o.mean()),
+                          "max_abs_lse": float(err_l.max())}), file=sys.stderr, flush=True)
+        del r
+        torch.cuda.empty_cache()
+
+
 def write_csv(path, header, rows):
     """The results file of the pages' benchmark assignment: one row per
     length with time and peak memory, "OOM" where a run ran out of memory."""
@@ -450,6 +496,9 @@ def main():
                     help="time the paged decode (attn_decode) on a decode workload")
     ap.add_argument("--compare", action="store_true",
                     help="time the kernel beside standard attention over the pages' length sweep")
+    ap.add_argument("--oracle-timings", action="store_true",
+                    help="also run the whole fp64 oracle on the host cores for the workloads it finishes in about a "
+                         "minute or less (one JSON line each, to stderr, with the GPU's median and minimum times)")
     ap.add_argument("--csv", default=None,
                     help="with --sweep or --compare, also write the per-length results (L, time_ms, mem_GB, "
                          "'OOM' where standard attention ran out of memory) to this CSV file")
@@ -517,9 +566,12 @@ def main():
     if args.data_sensitivity:
         data_sensitivity(w, r["inputs"], max(5, args.steps))
 
+    r = line = None  # the headline's tensors are no longer needed
+    torch.cuda.empty_cache()
+    if args.oracle_timings:
+        oracle_timings(max(10, args.steps))
+
     if args.sweep:
-        del r, line
-        torch.cuda.empty_cache()
         sweep = []
         for name, ws in WORKLOADS.items():
             rs = time_workload(ws, max(5, args.steps), 3)

@@ -406,6 +406,32 @@ def profiled_traffic(w, kind: str = "attn_fwd", source: str = KERNEL_SOURCE):
             + float(vals["write_kib_per_dispatch"]) * 1024 * write_scale)
 
 
+def profiled_request_traffic(w, kind: str = "attn_fwd", source: str = KERNEL_SOURCE):
+    """Bytes per launch between L2 and memory counted from the request-size
+    counters (TCC_EA0_RDREQ_32B/64B/128B and TCC_EA0_WRREQ/WRREQ_64B, each
+    request times its size), scaled by what the same counters read for a plain
+    device copy of known size; None when there is no summary for this workload
+    or the kernel source has changed since it was taken.  FETCH_SIZE estimates
+    128-byte reads from a bubble counter, and on gfx950 its ratio to the true
+    bytes differs between kernels with the same request sizes, so its copy
+    scaling is not exact; the request counts are."""
+    path = os.path.join(PROFILES, f"{kind}_{w.name}_requests.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            key, val = line.split("=", 1)
+            vals[key.strip()] = val.strip()
+    if vals.get("workload") != w.name or vals.get("kernel_source_sha256") != kernel_source_sha256(source):
+        return None
+    copy_bytes = float(vals["copy_bytes"])
+    read_scale = copy_bytes / float(vals["copy_read_bytes"])
+    write_scale = copy_bytes / float(vals["copy_write_bytes"])
+    return (float(vals["read_bytes_per_launch"]) * read_scale
+            + float(vals["write_bytes_per_launch"]) * write_scale)
+
+
 def roofline_block(w, ms):
     flops = algorithmic_flops(w)
     achieved = flops / (ms * 1e-3) / 1e12
@@ -413,7 +439,8 @@ def roofline_block(w, ms):
     source = KERNEL_SOURCE_F8 if w.dtype == "f8" else KERNEL_SOURCE
     return {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
             "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-            "traffic": profiled_traffic(w, "attn_fwd", source)}
+            "traffic": profiled_traffic(w, "attn_fwd", source),
+            "traffic_requests": profiled_request_traffic(w, "attn_fwd", source)}
 
 
 ORACLE_TIMING_WORKLOADS = ("p2_accuracy", "causal_4k", "noncausal_2k_f16", "noncausal_2k_bf16", "causal_8k",
@@ -748,6 +775,7 @@ def main_decode(w, args):
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": profiled_traffic(w, "attn_decode", KERNEL_SOURCE_DECODE),
+                     "traffic_requests": profiled_request_traffic(w, "attn_decode", KERNEL_SOURCE_DECODE),
                      "scope": "one attn_decode call (partial and merge kernels)"},
     }
     if not args.no_cpu_baseline:
@@ -780,6 +808,7 @@ def main_backward(w, args):
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_F16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_F16_TFLOPS, 4),
                      "traffic": profiled_traffic(w, "attn_bwd", KERNEL_SOURCE_BWD),
+                     "traffic_requests": profiled_request_traffic(w, "attn_bwd", KERNEL_SOURCE_BWD),
                      "scope": "one attn_bwd call (prep, dK/dV and dQ kernels)"},
     }
     if not args.no_cpu_baseline:

@@ -10,21 +10,29 @@
 // j <= p (and p - j <= window).
 //
 // Two kernels:
-//   1. partial (split-K): one wave owns a chunk of one sequence's keys for
-//      one K/V head and all query rows that read that head (up to 32 rows:
-//      the group's heads times Lq).  Each wave works alone -- its own LDS
-//      region, no barriers.  Per 32-key tile: the K rows go straight from the
-//      cache into the A-operand registers of S^T = K Q^T (16 contiguous bytes
-//      per lane), the V tile goes into LDS by direct-to-LDS loads (for the
-//      transposing read of the second product), both one tile ahead; the
-//      online softmax is per lane; the chunk's (max, sum, unnormalised O)
-//      go to the workspace.
-//   2. merge: one workgroup per query row combines its chunks exactly (the
-//      same rescale the online softmax uses) and writes O and lse.
+//   1. partial (split-K over an even partition): the work is the list of
+//      32-key tiles of every segment -- (sequence, K/V head, block of up to
+//      32 query rows that read that head: the group's heads times Lq) --
+//      laid end to end.  Each of W waves takes an equal run of P consecutive
+//      tiles; W is as many waves as the device holds at once, so all of them
+//      start at the launch and finish together (no later rounds of waves
+//      behind a tail of unequal chunks).  A run may start or end inside a
+//      segment and cross into the next ones; the wave writes one partial
+//      result (max, sum, unnormalised O) per segment it touches.  Each wave
+//      works alone -- its own LDS region, no barriers.  Per tile: the K rows
+//      go straight from the cache into the A-operand registers of S^T = K Q^T
+//      (16 contiguous bytes per lane), the V tile goes into LDS by
+//      direct-to-LDS loads (for the transposing read of the second product),
+//      both one tile ahead and the page-table entries two tiles ahead; the
+//      online softmax is per lane.
+//   2. merge: one workgroup per query row combines the partial results of the
+//      waves that touched its segment exactly (the same rescale the online
+//      softmax uses) and writes O and lse.
 // The products run on the 32x32x16 MFMA although at most Lq*H/H_kv of the
 // 32 query columns are live: the kernel is bound by bytes, not FLOPs.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -35,8 +43,11 @@
 
 namespace {
 
-constexpr int kDecTile = 32;  // keys per tile
-constexpr int kDecWaves = 4;  // independent waves per workgroup
+constexpr int kDecTile = 32;     // keys per tile
+constexpr int kDecWaves = 4;     // independent waves per workgroup
+constexpr int kMaxWaves = 4096;  // most waves of the partial kernel (bounds the workspace)
+constexpr int kMinTiles = 8;     // fewest tiles per wave
+constexpr int kMaxDevices = 64;
 constexpr float kLn2 = 0.69314718055994531f;
 
 struct DecParams {
@@ -44,17 +55,28 @@ struct DecParams {
     const int *table, *lens;
     void *o;
     float *lse;
-    float *part;        // [rows_total][n_chunks][D] unnormalised O, then [rows_total][n_chunks][2] (m, l)
+    int64_t *hdr;  // workspace head: [B + 1] first tile of each sequence in the list (the last = total), then P
+    float *part;   // [n_slots][rslot][D] unnormalised O, then [n_slots][rslot][2] (m, l)
     int B, H, H_kv, Lq, group, rows;  // rows = group * Lq: query rows per K/V head
     int d;                            // head size (host side: picks the kernel instance)
     int bs, bs_shift, max_blocks, num_blocks, max_len, window;
-    int chunk, n_chunks, n_rowblk, n_cgroups;
+    int n_rowblk, nseg, rslot;  // row blocks per K/V head; segments per sequence (H_kv * n_rowblk); rows per slot
+    int n_waves, n_slots;       // waves of the partial kernel; result slots (most waves + B * nseg)
     float scale_log2;
 };
 
+// Read through the constant address space: the lengths and the page table
+// are not written while the kernels run, so a wave-uniform read of them can be
+// a scalar load, which the wave's waits for its vector loads (vmcnt) do not
+// include.
+__device__ __forceinline__ int load_invariant(const int *ptr)
+{
+    return *(const __attribute__((address_space(4))) int *)ptr;
+}
+
 __device__ __forceinline__ int seq_len(const DecParams &p, int b)
 {
-    return min(max(p.lens[b], 0), p.max_len);
+    return min(max(load_invariant(p.lens + b), 0), p.max_len);
 }
 
 // First key any query row of a sequence of n tokens can see.
@@ -63,13 +85,86 @@ __device__ __forceinline__ int first_key(const DecParams &p, int n)
     return p.window >= 0 ? max(0, n - p.Lq - p.window) : 0;
 }
 
-// Physical block holding key j of sequence b (table entries and the block
-// number are clamped, so a bad table reads a wrong block, never out of bounds).
-__device__ __forceinline__ int64_t page_of(const DecParams &p, int b, int j)
+// Page-table entry for key j of sequence b (the logical block number is
+// clamped), and the physical block it names (the entry is clamped too, so a
+// bad table reads a wrong block, never out of bounds).
+__device__ __forceinline__ int table_entry(const DecParams &p, int b, int j)
 {
     const int lb = min(j >> p.bs_shift, p.max_blocks - 1);
-    const int phys = p.table[(int64_t)b * p.max_blocks + lb];
-    return min(max(phys, 0), p.num_blocks - 1);
+    return load_invariant(p.table + (int64_t)b * p.max_blocks + lb);
+}
+
+__device__ __forceinline__ int64_t physical_block(const DecParams &p, int entry)
+{
+    return min(max(entry, 0), p.num_blocks - 1);
+}
+
+// A position in the tile list: sequence b (n tokens, tiles [t_lo, t_hi) hold
+// every key one of its query rows can see), K/V head g, row block rb, tile t.
+struct Cursor {
+    int b, g, rb, t, t_lo, t_hi, n;
+};
+
+__device__ __forceinline__ void set_sequence(const DecParams &p, Cursor &c, int b)
+{
+    c.b = b;
+    c.n = seq_len(p, b);
+    c.t_lo = first_key(p, c.n) / kDecTile;
+    c.t_hi = (c.n + kDecTile - 1) / kDecTile;  // n = 0: no tile
+}
+
+// Tiles of sequence b over all its segments.
+__device__ __forceinline__ int64_t sequence_span(const DecParams &p, int b)
+{
+    Cursor c;
+    set_sequence(p, c, b);
+    return (int64_t)(c.t_hi - c.t_lo) * p.nseg;
+}
+
+// The tile after c (sequences without tiles are skipped; past the last tile
+// of the list the cursor stays inside the last sequence and is not used).
+__device__ __forceinline__ Cursor next_tile(const DecParams &p, Cursor c)
+{
+    if (++c.t < c.t_hi) return c;
+    c.t = c.t_lo;
+    if (++c.rb < p.n_rowblk) return c;
+    c.rb = 0;
+    if (++c.g < p.H_kv) return c;
+    c.g = 0;
+    while (c.b + 1 < p.B) {
+        set_sequence(p, c, c.b + 1);
+        if (c.t_hi > c.t_lo) break;
+    }
+    c.t = c.t_lo;
+    return c;
+}
+
+__device__ __forceinline__ int64_t uniform64(int64_t x)
+{
+    const uint64_t u = (uint64_t)x;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// s_waitcnt vmcnt(N): at most N of this wave's vector memory operations are
+// still outstanding (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int64_t wave_prefix_sum(int64_t x, int lane)
+{
+#pragma unroll
+    for (int off = 1; off < 64; off *= 2) {
+        const long long y = __shfl_up((long long)x, off);
+        if (lane >= off) x += y;
+    }
+    return x;
 }
 
 // ---------------------------------------------------------------- 1. partial
@@ -88,37 +183,59 @@ __global__ __launch_bounds__(64 * kDecWaves) void attn_decode_partial_kernel(Dec
     __shared__ __attribute__((aligned(16))) char lds_a[kDecWaves][kTileBytes];
     __shared__ __attribute__((aligned(16))) char lds_b[kDecWaves][kTileBytes];
 
-    const int wave = threadIdx.x / 64;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
     const int lane = threadIdx.x % 64;
     const int l32 = lane % 32;
     const int hi = lane / 32;
+    const int w = blockIdx.x * kDecWaves + wave;  // this wave's run of the tile list
+    if (w >= p.n_waves) return;
 
-    int idx = blockIdx.x;
-    const int cg = idx % p.n_cgroups;
-    idx /= p.n_cgroups;
-    const int rowblk = idx % p.n_rowblk;
-    idx /= p.n_rowblk;
-    const int g = idx % p.H_kv;
-    const int b = idx / p.H_kv;
-    const int c = __builtin_amdgcn_readfirstlane(cg * kDecWaves + wave);  // this wave's chunk
-    if (c >= p.n_chunks) return;
-    const int n = seq_len(p, b);
-    const int k_begin = max(c * p.chunk, first_key(p, n));
-    const int k_end = min(n, (c + 1) * p.chunk);
-    if (k_begin >= k_end) return;  // no key here: the merge skips this chunk
+    // ---- the tile list: each sequence's first tile in it, the total, the run length P
+    int64_t total = 0;
+    int64_t span0 = 0, incl0 = 0;  // sequences 0..63 (kept for the search below)
+    for (int b0 = 0; b0 < p.B; b0 += 64) {
+        const int b = b0 + lane;
+        const int64_t span = b < p.B ? sequence_span(p, b) : 0;
+        const int64_t incl = wave_prefix_sum(span, lane);
+        if (b0 == 0) {
+            span0 = span;
+            incl0 = incl;
+        }
+        if (w == 0 && b < p.B) p.hdr[b] = total + incl - span;
+        total += uniform64(__shfl((long long)incl, 63));
+    }
+    const int64_t P = max((total + p.n_waves - 1) / p.n_waves, (int64_t)kMinTiles);
+    if (w == 0 && lane == 0) {
+        p.hdr[p.B] = total;
+        p.hdr[p.B + 1] = P;
+    }
+    const int64_t f_begin = (int64_t)w * P;
+    const int64_t f_end = min(total, f_begin + P);
+    if (f_begin >= f_end) return;
 
-    // ---- this lane's query row: (head in group, new-token index)
-    const int r = rowblk * 32 + l32;
-    const bool row_live = r < p.rows;
-    const int hh = row_live ? r / p.Lq : 0;
-    const int qi = row_live ? r % p.Lq : 0;
-    const int h = g * p.group + hh;
-    const int pos = n - p.Lq + qi;  // its position (rows with pos < 0 see no key)
-    const T *qrow = static_cast<const T *>(p.q) + (((int64_t)b * p.H + h) * p.Lq + qi) * D;
-    vec8 qf[kDSteps];
-#pragma unroll
-    for (int s = 0; s < kDSteps; ++s)
-        qf[s] = row_live ? *reinterpret_cast<const vec8 *>(qrow + 16 * s + 8 * hi) : vec8{};
+    // ---- the cursor at f_begin: the sequence whose tiles hold it, then segment and tile
+    Cursor c0;
+    {
+        int64_t run = 0;
+        for (int b0 = 0; b0 < p.B; b0 += 64) {
+            const int b = b0 + lane;
+            const int64_t span = b0 == 0 ? span0 : b < p.B ? sequence_span(p, b) : 0;
+            const int64_t incl = b0 == 0 ? incl0 : wave_prefix_sum(span, lane);
+            const uint64_t found = __ballot(b < p.B && run + incl > f_begin);
+            if (found) {
+                const int l = __builtin_ctzll(found);
+                const int64_t off = f_begin - run - uniform64(__shfl((long long)(incl - span), l));
+                set_sequence(p, c0, b0 + l);
+                const int tiles = c0.t_hi - c0.t_lo;  // > 0: the sequence holds f_begin
+                const int seg = (int)(off / tiles);
+                c0.t = c0.t_lo + (int)(off % tiles);
+                c0.g = seg / p.n_rowblk;
+                c0.rb = seg % p.n_rowblk;
+                break;
+            }
+            run += uniform64(__shfl((long long)incl, 63));
+        }
+    }
 
     const T *kc = static_cast<const T *>(p.kc);
     const T *vc = static_cast<const T *>(p.vc);
@@ -132,31 +249,31 @@ __global__ __launch_bounds__(64 * kDecWaves) void attn_decode_partial_kernel(Dec
 #pragma unroll
     for (int cc = 0; cc < kHalfCopies; ++cc) ld_v[cc] = copy_src_offset<D, kSwzV>(cc * 64 + lane);
 
-    // The physical blocks of the two 16-key halves of tile t (wave-uniform).
-    // They are fetched two tiles ahead, so a tile's data loads never wait on
-    // a page-table load.
+    // The page-table entries of the two 16-key halves of a tile (wave-uniform
+    // scalar loads).  They are fetched two tiles ahead and clamped only where
+    // used, so a tile's data loads never wait on a page-table load.
     struct Pages { int lo, hi; };
-    auto pages_of = [&](int t) {
+    auto pages_of = [&](const Cursor &c) {
         Pages pg;
-        pg.lo = (int)page_of(p, b, t * kDecTile);
-        pg.hi = (int)page_of(p, b, t * kDecTile + 16);
+        pg.lo = table_entry(p, c.b, c.t * kDecTile);
+        pg.hi = table_entry(p, c.b, c.t * kDecTile + 16);
         return pg;
     };
-    // K fragments of tile t into registers; V tile t into this wave's stage
-    auto load_k = [&](int t, Pages pg, vec8 (&kf)[kDSteps]) {
-        const int j = t * kDecTile + krow;  // krow < 16 exactly when l32 < 16
-        const int64_t page = l32 < 16 ? pg.lo : pg.hi;
-        const T *row = kc + ((page * p.H_kv + g) * p.bs + (j & (p.bs - 1))) * D;
+    // K fragments of a tile into registers; its V tile into this wave's stage
+    auto load_k = [&](const Cursor &c, Pages pg, vec8 (&kf)[kDSteps]) {
+        const int j = c.t * kDecTile + krow;  // krow < 16 exactly when l32 < 16
+        const int64_t page = physical_block(p, l32 < 16 ? pg.lo : pg.hi);
+        const T *row = kc + ((page * p.H_kv + c.g) * p.bs + (j & (p.bs - 1))) * D;
 #pragma unroll
         for (int s = 0; s < kDSteps; ++s) kf[s] = *reinterpret_cast<const vec8 *>(row + 16 * s + 8 * hi);
     };
-    auto copy_v = [&](int t, Pages pg, char *stage) {
+    auto copy_v = [&](const Cursor &c, Pages pg, char *stage) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-            const int j0 = t * kDecTile + 16 * hf;
-            const int valid = min(max(n - j0, 0), 16);  // rows past n arrive as zeros
-            const int64_t page = __builtin_amdgcn_readfirstlane(hf ? pg.hi : pg.lo);
-            const T *base = vc + ((page * p.H_kv + g) * p.bs + (j0 & (p.bs - 1))) * D;
+            const int j0 = c.t * kDecTile + 16 * hf;
+            const int valid = min(max(c.n - j0, 0), 16);  // rows past n arrive as zeros
+            const int64_t page = physical_block(p, __builtin_amdgcn_readfirstlane(hf ? pg.hi : pg.lo));
+            const T *base = vc + ((page * p.H_kv + c.g) * p.bs + (j0 & (p.bs - 1))) * D;
             const __amdgpu_buffer_rsrc_t rv =
                 __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, valid * kRowBytes, 0x00020000);
 #pragma unroll
@@ -165,21 +282,73 @@ __global__ __launch_bounds__(64 * kDecWaves) void attn_decode_partial_kernel(Dec
         }
     };
 
+    // ---- the segment being accumulated and this lane's query row in it
+    int seg_b = -1, seg_g = 0, seg_rb = 0;  // wave-uniform
+    int k_begin = 0, k_end = 0, min_pos = 0, max_pos = 0;
+    bool row_live = false;
+    int pos = 0;
+    vec8 qf[kDSteps];
     f32x16 acc_o[kDBlocks];
-#pragma unroll
-    for (int i = 0; i < kDBlocks; ++i) acc_o[i] = f32x16{};
     float m_run = -INFINITY;  // running max of scale*log2(e)*s
     float l_run = 0.f;        // running sum of weights, this lane half's keys
 
-    const int t_first = k_begin / kDecTile;
-    const int t_last = (k_end + kDecTile - 1) / kDecTile;  // one past
-    const int max_pos = n - 1;
-    const int min_pos = n - p.Lq;
-    char *stage_a = lds_a[wave];
-    char *stage_b = lds_b[wave];
+    // the segment's partial result into slot w + (its index among all segments)
+    auto flush = [&]() {
+        const float l_tot = half_swap_sum(l_run);
+        if (!row_live) return;
+        const int64_t slot = (int64_t)w + ((int64_t)seg_b * p.H_kv + seg_g) * p.n_rowblk + seg_rb;
+        float *po = p.part + (slot * p.rslot + l32) * D;
+#pragma unroll
+        for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                // register 4a+cc of block db holds d = 32db + 8a + 4hi + cc
+                const float4 v4 = {acc_o[db][4 * a], acc_o[db][4 * a + 1], acc_o[db][4 * a + 2], acc_o[db][4 * a + 3]};
+                *reinterpret_cast<float4 *>(po + 32 * db + 8 * a + 4 * hi) = v4;
+            }
+        if (hi == 0) {
+            float *pml = p.part + (int64_t)p.n_slots * p.rslot * D + 2 * (slot * p.rslot + l32);
+            pml[0] = m_run;
+            pml[1] = l_tot;
+        }
+    };
+    // start accumulating the segment of cursor c
+    auto begin_segment = [&](const Cursor &c) {
+        seg_b = c.b;
+        seg_g = c.g;
+        seg_rb = c.rb;
+        const int r = c.rb * 32 + l32;  // row (head in group, new-token index) of this lane
+        row_live = r < p.rows;
+        const int hh = row_live ? r / p.Lq : 0;
+        const int qi = row_live ? r % p.Lq : 0;
+        const int h = c.g * p.group + hh;
+        pos = c.n - p.Lq + qi;  // its position (rows with pos < 0 see no key)
+        k_begin = first_key(p, c.n);
+        k_end = c.n;
+        max_pos = c.n - 1;
+        min_pos = c.n - p.Lq;
+        const T *qrow = static_cast<const T *>(p.q) + (((int64_t)c.b * p.H + h) * p.Lq + qi) * D;
+#pragma unroll
+        for (int s = 0; s < kDSteps; ++s)
+            qf[s] = row_live ? *reinterpret_cast<const vec8 *>(qrow + 16 * s + 8 * hi) : vec8{};
+        // Wait for them here (and for every load before them), and hide their
+        // origin from the compiler: the products of every tile then wait only
+        // for that tile's own loads, not for a query load on some other path.
+        wait_vmcnt<0>();
+#pragma unroll
+        for (int s = 0; s < kDSteps; ++s) asm volatile("" : "+v"(qf[s]));
+#pragma unroll
+        for (int i = 0; i < kDBlocks; ++i) acc_o[i] = f32x16{};
+        m_run = -INFINITY;
+        l_run = 0.f;
+    };
 
-    auto process = [&](int t, const vec8 (&kf)[kDSteps], const char *tv) {
-        const int j0 = t * kDecTile;
+    auto process = [&](const Cursor &c, const vec8 (&kf)[kDSteps], const char *tv) {
+        if (c.b != seg_b || c.g != seg_g || c.rb != seg_rb) {
+            if (seg_b >= 0) flush();
+            begin_segment(c);
+        }
+        const int j0 = c.t * kDecTile;
         // S^T = K Q^T: register r holds key j0 + 16(r/8) + 8hi + r%8 of this lane's row
         f32x16 s = f32x16{};
 #pragma unroll
@@ -231,115 +400,174 @@ __global__ __launch_bounds__(64 * kDecWaves) void attn_decode_partial_kernel(Dec
             }
     };
 
-    // two tiles in flight: loads of tile t+1 overlap the products of tile t.
-    // The wave waits for its own loads only (vmcnt); before a copy reuses a
-    // stage, its reads of that stage have completed (lgkmcnt).
+    // Two tiles in flight: the loads of tile f+1 are issued before the wave
+    // waits for tile f, and overlap its products.  The wave waits for its own
+    // loads only (vmcnt, in issue order: all but the kTileLoads newest); before
+    // a copy reuses a stage, its reads of that stage have completed (lgkmcnt).
+    // Every step issues one tile's loads whether or not a tile is left (past
+    // the end of the run it loads the tile just processed again, which is
+    // still in L2), so every path through the loop has the same loads in
+    // flight and the compiler's own waits stay as loose as the ones here.
+    // At the top of each step c0 is tile f (in stage a), c1 tile f+1, c2 tile
+    // f+2, pg0 and pg1 the page entries of c0 and c1.
+    constexpr int kTileLoads = kDSteps + 2 * kHalfCopies;  // vector memory instructions per tile
+    char *stage_a = lds_a[wave];
+    char *stage_b = lds_b[wave];
     vec8 kf_a[kDSteps], kf_b[kDSteps];
-    Pages pg_next = pages_of(t_first + 1 < t_last ? t_first + 1 : t_first);
-    {
-        const Pages pg0 = pages_of(t_first);
-        load_k(t_first, pg0, kf_a);
-        copy_v(t_first, pg0, stage_a);
-    }
-    for (int t = t_first; t < t_last; t += 2) {
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-        if (t + 1 < t_last) {
-            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-            load_k(t + 1, pg_next, kf_b);
-            copy_v(t + 1, pg_next, stage_b);
-            if (t + 2 < t_last) pg_next = pages_of(t + 2);
-        }
-        process(t, kf_a, stage_a);
-        if (t + 1 < t_last) {
-            __builtin_amdgcn_s_waitcnt(0x0F70);
-            if (t + 2 < t_last) {
-                __builtin_amdgcn_s_waitcnt(0xC07F);
-                load_k(t + 2, pg_next, kf_a);
-                copy_v(t + 2, pg_next, stage_a);
-                if (t + 3 < t_last) pg_next = pages_of(t + 3);
-            }
-            process(t + 1, kf_b, stage_b);
-        }
-    }
+    Cursor c1 = next_tile(p, c0);  // past the end of the run: a tile inside the list, not processed
+    Cursor c2 = next_tile(p, c1);
+    Pages pg0 = pages_of(c0);
+    Pages pg1 = pages_of(c1);
+    load_k(c0, pg0, kf_a);
+    copy_v(c0, pg0, stage_a);
+    begin_segment(c0);  // its query rows load while the first tile is in flight
+    for (int64_t f = f_begin; f < f_end; f += 2) {
+        const bool has1 = f + 1 < f_end;
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        load_k(has1 ? c1 : c0, has1 ? pg1 : pg0, kf_b);
+        copy_v(has1 ? c1 : c0, has1 ? pg1 : pg0, stage_b);
+        const Pages pg2 = pages_of(c2);
+        wait_vmcnt<kTileLoads>();
+        process(c0, kf_a, stage_a);
+        if (!has1) break;
 
-    // ---- this chunk's partial result: unnormalised O, max, sum
-    if (!row_live) return;
-    const int64_t pr = (((int64_t)b * p.H + h) * p.Lq + qi) * p.n_chunks + c;
-    const int64_t rows_total = (int64_t)p.B * p.H * p.Lq;
-    float *po = p.part + pr * D;
-#pragma unroll
-    for (int db = 0; db < kDBlocks; ++db)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            // register 4a+cc of block db holds d = 32db + 8a + 4hi + cc
-            const float4 v4 = {acc_o[db][4 * a], acc_o[db][4 * a + 1], acc_o[db][4 * a + 2], acc_o[db][4 * a + 3]};
-            *reinterpret_cast<float4 *>(po + 32 * db + 8 * a + 4 * hi) = v4;
-        }
-    const float l_tot = half_swap_sum(l_run);
-    if (hi == 0) {
-        float *pml = p.part + rows_total * p.n_chunks * D + 2 * pr;
-        pml[0] = m_run;
-        pml[1] = l_tot;
+        const bool has2 = f + 2 < f_end;
+        const Cursor c3 = next_tile(p, c2);
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        load_k(has2 ? c2 : c1, has2 ? pg2 : pg1, kf_a);
+        copy_v(has2 ? c2 : c1, has2 ? pg2 : pg1, stage_a);
+        const Pages pg3 = pages_of(c3);
+        wait_vmcnt<kTileLoads>();
+        process(c1, kf_b, stage_b);
+        c0 = c2;
+        pg0 = pg2;
+        c1 = c3;
+        pg1 = pg3;
+        c2 = next_tile(p, c3);
     }
+    wait_vmcnt<0>();  // no copy into LDS outlives the wave
+    flush();
 }
 
 // ---------------------------------------------------------------- 2. merge
-// One workgroup of 4 waves per query row: every thread takes a share of the
-// chunks' maxima, the block agrees on the largest M, then wave w sums the
-// chunks c = w, w+4, ... with weights 2^(m_c - M) (lanes over d) and the
-// four partial sums meet in LDS.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void attn_decode_merge_kernel(DecParams p)
+// One workgroup of NW waves per query row.  The waves of the partial kernel
+// whose runs met the row's segment are w_lo..w_hi (the runs are consecutive
+// and equal): every thread takes a share of their maxima, the block agrees
+// on the largest M, then the waves sum the results with weights 2^(m_w - M)
+// and the NW partial sums meet in LDS, added in wave order.  A row with few
+// results (many short segments) gets 4 waves, each taking one result per
+// load; a row with many (few long segments) 16 waves, each taking several
+// results per load.
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_decode_merge_kernel(DecParams p)
 {
-    constexpr int kPer = D / 64;  // elements of O per lane
-    __shared__ float red_m[4];
-    __shared__ float red_o[4][D + 1];
+    __shared__ float red_m[NW];
+    __shared__ float red_o[NW][D + 1];
     const int wave = threadIdx.x / 64;
     const int lane = threadIdx.x % 64;
-    const int64_t rows_total = (int64_t)p.B * p.H * p.Lq;
     const int64_t row = blockIdx.x;  // (b*H + h)*Lq + i
     const int b = (int)(row / ((int64_t)p.H * p.Lq));
+    const int h = (int)(row / p.Lq % p.H);
     const int i = (int)(row % p.Lq);
-    const int n = seq_len(p, b);
-    const int pos = n - p.Lq + i;
-    const int c_first = first_key(p, n) / p.chunk;
-    const int c_last = (pos >= 0 && n > 0) ? (n - 1) / p.chunk : c_first - 1;  // empty when pos < 0
-    const float *pml = p.part + rows_total * p.n_chunks * D + 2 * row * p.n_chunks;
-    const float *po = p.part + row * p.n_chunks * D;
+    const int g = h / p.group;
+    const int r = (h % p.group) * p.Lq + i;  // row within the K/V head's rows
+    const int rb = r / 32;
+    const int seg = g * p.n_rowblk + rb;      // segment within the sequence
+    const int64_t seq_first = p.hdr[b];
+    const int64_t tiles = (p.hdr[b + 1] - seq_first) / p.nseg;  // tiles of each segment of sequence b
+    const int64_t P = p.hdr[p.B + 1];
+    int64_t w_lo = 0, w_hi = -1;  // none when the sequence has no tile
+    if (tiles > 0) {
+        const int64_t f_seg = seq_first + seg * tiles;
+        w_lo = f_seg / P;
+        w_hi = (f_seg + tiles - 1) / P;
+    }
+    const int64_t slot0 = (int64_t)b * p.nseg + seg;  // wave w's result for this segment: slot w + slot0
+    const int64_t rs = r % 32;
+    const float *pml = p.part + (int64_t)p.n_slots * p.rslot * D;
 
     float m = -INFINITY;
-    for (int c = c_first + (int)threadIdx.x; c <= c_last; c += 256) m = fmaxf(m, pml[2 * c]);
+    for (int64_t w = w_lo + threadIdx.x; w <= w_hi; w += 64 * NW) m = fmaxf(m, pml[2 * ((w + slot0) * p.rslot + rs)]);
 #pragma unroll
     for (int off = 32; off > 0; off /= 2) m = fmaxf(m, __shfl_xor(m, off));
     if (lane == 0) red_m[wave] = m;
     __syncthreads();
-    m = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+    m = red_m[0];
+#pragma unroll
+    for (int v = 1; v < NW; ++v) m = fmaxf(m, red_m[v]);
 
-    float l = 0.f, acc[kPer];
+    float l = 0.f;
+    if constexpr (NW == 4) {
+        // wave v takes the results w_lo + v, + 4, ... (one per load, lanes over d)
+        constexpr int kPer = D / 64;
+        float acc[kPer];
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
-    if (m != -INFINITY) {
+        for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
+        if (m != -INFINITY) {
 #pragma unroll 4
-        for (int c = c_first + wave; c <= c_last; c += 4) {
-            const float mc = pml[2 * c];
-            const float w = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - m);
-            l += w * pml[2 * c + 1];
+            for (int64_t w = w_lo + wave; w <= w_hi; w += NW) {
+                const int64_t sr = (w + slot0) * p.rslot + rs;
+                const float mc = pml[2 * sr];
+                const float wt = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - m);
+                l += wt * pml[2 * sr + 1];
 #pragma unroll
-            for (int e = 0; e < kPer; ++e) acc[e] += w * po[(int64_t)c * D + e * 64 + lane];
+                for (int e = 0; e < kPer; ++e) acc[e] += wt * p.part[sr * D + e * 64 + lane];
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) red_o[wave][e * 64 + lane] = acc[e];
+    } else {
+        // lanes over (result, 4 consecutive d): a wave reads 64 / (D / 4)
+        // results per load, 16 bytes per lane, and sums them up the lane bits
+        // above d
+        constexpr int kLanesPerPart = D / 4;
+        constexpr int kPartsPerWave = 64 / kLanesPerPart;
+        const int sub = lane / kLanesPerPart;
+        const int d4 = lane % kLanesPerPart;
+        float4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (m != -INFINITY) {
+#pragma unroll 4
+            for (int64_t w = w_lo + wave * kPartsPerWave + sub; w <= w_hi; w += NW * kPartsPerWave) {
+                const int64_t sr = (w + slot0) * p.rslot + rs;
+                const float mc = pml[2 * sr];
+                const float wt = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - m);
+                if (d4 == 0) l += wt * pml[2 * sr + 1];
+                const float4 v = *reinterpret_cast<const float4 *>(p.part + sr * D + 4 * d4);
+                acc.x += wt * v.x;
+                acc.y += wt * v.y;
+                acc.z += wt * v.z;
+                acc.w += wt * v.w;
+            }
+        }
+#pragma unroll
+        for (int off = kLanesPerPart; off < 64; off *= 2) {
+            acc.x += __shfl_xor(acc.x, off);
+            acc.y += __shfl_xor(acc.y, off);
+            acc.z += __shfl_xor(acc.z, off);
+            acc.w += __shfl_xor(acc.w, off);
+            l += __shfl_xor(l, off);
+        }
+        if (lane < kLanesPerPart) {
+            red_o[wave][4 * d4] = acc.x;
+            red_o[wave][4 * d4 + 1] = acc.y;
+            red_o[wave][4 * d4 + 2] = acc.z;
+            red_o[wave][4 * d4 + 3] = acc.w;
         }
     }
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) red_o[wave][e * 64 + lane] = acc[e];
     if (lane == 0) red_o[wave][D] = l;
     __syncthreads();
     if (wave != 0) return;
-    l = (red_o[0][D] + red_o[1][D]) + (red_o[2][D] + red_o[3][D]);
+    l = 0.f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) l += red_o[v][D];
     const float inv = l > 0.f ? 1.f / l : 0.f;
     T *orow = static_cast<T *>(p.o) + row * D;
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) {
+    for (int e = 0; e < D / 64; ++e) {
         const int d = e * 64 + lane;
-        const float o = (red_o[0][d] + red_o[1][d]) + (red_o[2][d] + red_o[3][d]);
+        float o = 0.f;
+#pragma unroll
+        for (int v = 0; v < NW; ++v) o += red_o[v][d];
         orow[d] = (T)(o * inv);
     }
     if (lane == 0) p.lse[row] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
@@ -347,38 +575,83 @@ __global__ __launch_bounds__(256) void attn_decode_merge_kernel(DecParams p)
 
 // ------------------------------------------------------------------ host side
 
-// Keys per wave chunk: enough chunks for ~8192 waves over the batch, at least
-// 256 keys (8 tiles) so the partial write stays small next to the keys read.
-int decode_chunk(int64_t B, int64_t H_kv, int64_t n_rowblk, int64_t max_len)
+struct DecodeShape {
+    int64_t rows, n_rowblk, nseg, rslot, waves_cap, n_slots;
+};
+
+// Row blocks, segments and the most waves a call of this shape can use (one
+// wave per kMinTiles tiles of the longest possible list, at most kMaxWaves);
+// each wave writes at most one result per segment it touches, and the runs
+// are consecutive, so waves_cap + B * nseg slots hold them all.
+DecodeShape decode_shape(int64_t B, int64_t H, int64_t H_kv, int64_t Lq, int64_t max_len)
 {
-    const int64_t target = 8192;
-    int64_t c = (max_len * B * H_kv * n_rowblk + target - 1) / target;
-    c = (c + kDecTile - 1) / kDecTile * kDecTile;
-    return (int)std::min<int64_t>(std::max<int64_t>(c, 256), 1 << 20);
+    DecodeShape s;
+    s.rows = H / H_kv * Lq;
+    s.n_rowblk = (s.rows + 31) / 32;
+    s.nseg = H_kv * s.n_rowblk;
+    s.rslot = std::min<int64_t>(s.rows, 32);
+    const int64_t tiles = B * s.nseg * ((max_len + kDecTile - 1) / kDecTile);
+    s.waves_cap = std::max<int64_t>(1, std::min<int64_t>(kMaxWaves, (tiles + kMinTiles - 1) / kMinTiles));
+    s.n_slots = s.waves_cap + B * s.nseg;
+    return s;
+}
+
+size_t decode_hdr_bytes(int64_t B)
+{
+    return (size_t)((B + 2) * 8 + 15) / 16 * 16;
 }
 
 size_t decode_workspace_bytes(int64_t B, int64_t H, int64_t H_kv, int64_t Lq, int d, int64_t max_len)
 {
-    const int64_t rows = H / H_kv * Lq;
-    const int64_t n_rowblk = (rows + 31) / 32;
-    const int64_t chunk = decode_chunk(B, H_kv, n_rowblk, max_len);
-    const int64_t n_chunks = (max_len + chunk - 1) / chunk;
-    return (size_t)(B * H * Lq * n_chunks * (d + 2) * (int64_t)sizeof(float));
+    const DecodeShape s = decode_shape(B, H, H_kv, Lq, max_len);
+    const size_t part = (size_t)(s.n_slots * s.rslot * (d + 2) * (int64_t)sizeof(float));
+    return (decode_hdr_bytes(B) + part + 15) / 16 * 16;
+}
+
+// Waves of the partial kernel the current device holds at once (queried
+// once per device and kernel instance); 0 when the query fails.
+std::mutex g_capacity_mutex;
+
+template <typename T, int D>
+int resident_waves()
+{
+    static int cached[kMaxDevices];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    std::lock_guard<std::mutex> lock(g_capacity_mutex);
+    if (!cached[dev]) {
+        int cus = 0, blocks = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &blocks, reinterpret_cast<const void *>(&attn_decode_partial_kernel<T, D>), 64 * kDecWaves, 0) !=
+                hipSuccess ||
+            cus < 1 || blocks < 1)
+            return 0;
+        cached[dev] = cus * blocks * kDecWaves;
+    }
+    return cached[dev];
 }
 
 template <typename T, int D>
 hipError_t launch_decode(DecParams p, hipStream_t stream)
 {
+    const int resident = resident_waves<T, D>();
+    if (resident < 1) return hipErrorInvalidDevice;
+    p.n_waves = std::min(p.n_waves, resident);  // n_slots keeps the workspace layout of the cap
     void *kargs[] = {&p};
-    const int64_t grid1 = (int64_t)p.B * p.H_kv * p.n_rowblk * p.n_cgroups;
+    const int grid1 = (p.n_waves + kDecWaves - 1) / kDecWaves;
     hipError_t err = hipLaunchKernel(reinterpret_cast<const void *>(&attn_decode_partial_kernel<T, D>),
                                      dim3((unsigned)grid1), dim3(64 * kDecWaves), kargs, 0, stream);
     if (err != hipSuccess) return err;
+    // a row has at most about n_waves / (B * nseg) + 1 partial results (fewer
+    // when the sequences are shorter than max_seq_len)
     const int64_t rows_total = (int64_t)p.B * p.H * p.Lq;
-    return hipLaunchKernel(reinterpret_cast<const void *>(&attn_decode_merge_kernel<T, D>),
-                           dim3((unsigned)rows_total), dim3(256), kargs, 0, stream);
+    if (p.n_waves >= (int64_t)128 * p.B * p.nseg)
+        return hipLaunchKernel(reinterpret_cast<const void *>(&attn_decode_merge_kernel<T, D, 16>),
+                               dim3((unsigned)rows_total), dim3(64 * 16), kargs, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void *>(&attn_decode_merge_kernel<T, D, 4>),
+                           dim3((unsigned)rows_total), dim3(64 * 4), kargs, 0, stream);
 }
-
 // Checks every argument but the workspace and fills the launch parameters
 // (all but p->part); *bytes_ws receives the workspace the call needs.  Makes
 // no HIP call.  ATTN_OK with p->B == 0 is an empty problem.
@@ -412,12 +685,9 @@ int decode_plan(const void *q, const void *k_cache, const void *v_cache, const i
     const unsigned __int128 q_elems = (unsigned __int128)B * H * Lq * d;
     if (cache_elems * sizeof(T) >= ((unsigned __int128)1 << 62) || q_elems * 16 >= ((unsigned __int128)1 << 62))
         return ATTN_ERR_SIZE;
-    const int rows = H / H_kv * Lq;
-    const int n_rowblk = (rows + 31) / 32;
-    const int chunk = decode_chunk(B, H_kv, n_rowblk, max_seq_len);
-    const int n_chunks = (max_seq_len + chunk - 1) / chunk;
-    const int n_cgroups = (n_chunks + kDecWaves - 1) / kDecWaves;
-    if ((int64_t)B * H_kv * n_rowblk * n_cgroups > INT_MAX || (int64_t)B * H * Lq > INT_MAX)
+    const DecodeShape sh = decode_shape(B, H, H_kv, Lq, max_seq_len);
+    if (sh.n_slots * sh.rslot * (d + 2) > (int64_t)1 << 40 || (int64_t)B * H * Lq > INT_MAX ||
+        B * sh.nseg > INT_MAX / 2)
         return ATTN_ERR_SIZE;
 
     const size_t bytes_q = (size_t)(q_elems * sizeof(T));
@@ -444,23 +714,25 @@ int decode_plan(const void *q, const void *k_cache, const void *v_cache, const i
     p.lens = seq_lens;
     p.o = out;
     p.lse = lse;
+    p.hdr = nullptr;
     p.part = nullptr;
     p.B = B;
     p.H = H;
     p.H_kv = H_kv;
     p.Lq = Lq;
     p.group = H / H_kv;
-    p.rows = rows;
+    p.rows = (int)sh.rows;
     p.bs = block_size;
     p.bs_shift = __builtin_ctz((unsigned)block_size);
     p.max_blocks = max_blocks;
     p.num_blocks = num_blocks;
     p.max_len = max_seq_len;
     p.window = window;
-    p.chunk = chunk;
-    p.n_chunks = n_chunks;
-    p.n_rowblk = n_rowblk;
-    p.n_cgroups = n_cgroups;
+    p.n_rowblk = (int)sh.n_rowblk;
+    p.nseg = (int)sh.nseg;
+    p.rslot = (int)sh.rslot;
+    p.n_waves = (int)sh.waves_cap;
+    p.n_slots = (int)sh.n_slots;
     p.scale_log2 = attn_resolve_scale(scale, d) * 1.4426950408889634f;
     p.d = d;
     return ATTN_OK;
@@ -494,7 +766,8 @@ int attn_decode_impl(const void *q, const void *k_cache, const void *v_cache, co
                                   (size_t)B * sizeof(int), bytes_q, (size_t)B * H * Lq * sizeof(float)};
     for (int j = 0; j < 7; ++j)
         if (overlaps(workspace, bytes_ws, others[j], other_bytes[j])) return ATTN_ERR_ALIAS;
-    p.part = static_cast<float *>(workspace);
+    p.hdr = static_cast<int64_t *>(workspace);
+    p.part = reinterpret_cast<float *>(static_cast<char *>(workspace) + decode_hdr_bytes(B));
     return decode_launch<T>(p, stream);
 }
 
@@ -511,7 +784,6 @@ static __device__ __align__(256) char scratch[kDecodeScratchBytes];
 
 namespace {
 
-constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mutex;
 void *g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once looked up
 
@@ -550,7 +822,8 @@ int attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
     void *ws = nullptr;
     const int sp = scratch_pointer(&ws);
     if (sp != ATTN_OK) return sp;
-    p.part = static_cast<float *>(ws);
+    p.hdr = static_cast<int64_t *>(ws);
+    p.part = reinterpret_cast<float *>(static_cast<char *>(ws) + decode_hdr_bytes(B));
     return decode_launch<_Float16>(p, stream);
 }
 

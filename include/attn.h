@@ -184,12 +184,16 @@ size_t attn_bwd_workspace_size(int B, int H, int L);
  *   seq_lens        : int32 [B], device memory; values are clamped to [0, max_seq_len]
  *   lse             : [B, H, Lq] fp32, natural log
  *   workspace       : attn_decode_workspace_size(B, H, H_kv, Lq, d, max_seq_len) bytes
- *                     (per-chunk partial results; contents undefined on return)
+ *                     (per-sequence offsets and partial results of the split
+ *                     over keys; contents undefined on return)
  * block_size: a power of two in [16, 4096]; max_seq_len <= max_blocks_per_seq *
  * block_size.  Table entries are clamped to [0, num_blocks - 1], so an
  * invalid table reads wrong blocks but never outside the cache.
  * Behaviour as for attn_fwd (device pointers, enqueue only, no allocation, no
  * synchronisation, arguments checked before any HIP call; B = 0 is empty).
+ * The keys are split evenly over as many waves as the device holds at once;
+ * the first call on a device asks the runtime for that number (the device
+ * current at the call, which must be the stream's device).
  * out, lse and workspace must not overlap one another or any input; q, the
  * caches, out and workspace 16-byte aligned, the int32 arrays and lse 4-byte.
  */
@@ -211,7 +215,7 @@ size_t attn_decode_workspace_size(int B, int H, int H_kv, int Lq, int d, int max
 /* attn_decode (fp16) for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc.  The same arguments as attn_decode without `workspace`: the
- * per-chunk partial results go to a static device array of 64 MiB
+ * offsets and partial results go to a static device array of 64 MiB
  * (67108864 bytes) that the library holds
  * on every device it runs on until the process ends; the call allocates
  * nothing.  A call whose attn_decode_workspace_size(...) exceeds it returns

@@ -268,8 +268,8 @@ def test_decode_noalloc_argument_errors():
     assert call_noalloc(o=DQ_) == attn.ATTN_ERR_ALIAS
     assert call_noalloc(q=DQ_ + 8) == attn.ATTN_ERR_ALIGN
     assert call_noalloc(q=0, kc=0, vc=0, bt=0, sl=0, o=0, lse=0, B=0) == attn.ATTN_OK
-    # 8 query rows per K/V head over 128k-token sequences need 130 MiB of
-    # partial results; 16 MiB for one new token each
+    # 8 new tokens per sequence (32 query rows per K/V head) need 73 MiB of
+    # partial results; one new token each, 8 MiB
     limit = 64 << 20
     big = dict(B=64, H=32, H_kv=8, Lq=8, d=128, bs=16, max_blocks=8192, num_blocks=8192, max_len=131072)
     assert attn.attn_decode_workspace_size(64, 32, 8, 8, 128, 131072) > limit

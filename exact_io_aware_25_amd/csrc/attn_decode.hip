@@ -452,9 +452,10 @@ __global__ __launch_bounds__(64 * kDecWaves) void attn_decode_partial_kernel(Dec
 // ---------------------------------------------------------------- 2. merge
 // One workgroup of NW waves per query row.  The waves of the partial kernel
 // whose runs met the row's segment are w_lo..w_hi (the runs are consecutive
-// and equal): every thread takes a share of their maxima, the block agrees
-// on the largest M, then the waves sum the results with weights 2^(m_w - M)
-// and the NW partial sums meet in LDS, added in wave order.  A row with few
+// and equal).  The merge is the online softmax's rescale over their results
+// (max m_w, sum l_w, unnormalised O_w): in one pass, each lane keeps a running
+// state, the states meet across lanes and then across waves in LDS (in wave
+// order), each rescaled by 2^(m - M) to the largest maximum M.  A row with few
 // results (many short segments) gets 4 waves, each taking one result per
 // load; a row with many (few long segments) 16 waves, each taking several
 // results per load.
@@ -465,10 +466,10 @@ __global__ __launch_bounds__(64 * NW) void attn_decode_merge_kernel(DecParams p)
     __shared__ float red_o[NW][D + 1];
     const int wave = threadIdx.x / 64;
     const int lane = threadIdx.x % 64;
-    const int64_t row = blockIdx.x;  // (b*H + h)*Lq + i
-    const int b = (int)(row / ((int64_t)p.H * p.Lq));
-    const int h = (int)(row / p.Lq % p.H);
-    const int i = (int)(row % p.Lq);
+    const int row = blockIdx.x;  // (b*H + h)*Lq + i (B*H*Lq < 2^31)
+    const int b = row / (p.H * p.Lq);
+    const int h = row / p.Lq % p.H;
+    const int i = row % p.Lq;
     const int g = h / p.group;
     const int r = (h % p.group) * p.Lq + i;  // row within the K/V head's rows
     const int rb = r / 32;
@@ -486,66 +487,75 @@ __global__ __launch_bounds__(64 * NW) void attn_decode_merge_kernel(DecParams p)
     const int64_t rs = r % 32;
     const float *pml = p.part + (int64_t)p.n_slots * p.rslot * D;
 
-    float m = -INFINITY;
-    for (int64_t w = w_lo + threadIdx.x; w <= w_hi; w += 64 * NW) m = fmaxf(m, pml[2 * ((w + slot0) * p.rslot + rs)]);
-#pragma unroll
-    for (int off = 32; off > 0; off /= 2) m = fmaxf(m, __shfl_xor(m, off));
-    if (lane == 0) red_m[wave] = m;
-    __syncthreads();
-    m = red_m[0];
-#pragma unroll
-    for (int v = 1; v < NW; ++v) m = fmaxf(m, red_m[v]);
-
-    float l = 0.f;
+    // One pass over the results: each lane keeps a running (max, sum, O) and
+    // rescales it when a larger maximum arrives, as the online softmax does;
+    // the running states then meet across lanes and waves the same way.
+    float m = -INFINITY, l = 0.f;
     if constexpr (NW == 4) {
         // wave v takes the results w_lo + v, + 4, ... (one per load, lanes over d)
         constexpr int kPer = D / 64;
         float acc[kPer];
 #pragma unroll
         for (int e = 0; e < kPer; ++e) acc[e] = 0.f;
-        if (m != -INFINITY) {
 #pragma unroll 4
-            for (int64_t w = w_lo + wave; w <= w_hi; w += NW) {
-                const int64_t sr = (w + slot0) * p.rslot + rs;
-                const float mc = pml[2 * sr];
-                const float wt = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - m);
-                l += wt * pml[2 * sr + 1];
+        for (int64_t w = w_lo + wave; w <= w_hi; w += NW) {
+            const int64_t sr = (w + slot0) * p.rslot + rs;
+            const float mc = pml[2 * sr];
+            const float lc = pml[2 * sr + 1];
+            float o[kPer];
 #pragma unroll
-                for (int e = 0; e < kPer; ++e) acc[e] += wt * p.part[sr * D + e * 64 + lane];
-            }
+            for (int e = 0; e < kPer; ++e) o[e] = p.part[sr * D + e * 64 + lane];
+            // no branch, so the loads of the unrolled iterations issue together
+            const float mn = fmaxf(m, mc);
+            const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+            const float wt = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - mn);
+            l = alpha * l + wt * lc;
+#pragma unroll
+            for (int e = 0; e < kPer; ++e) acc[e] = alpha * acc[e] + wt * o[e];
+            m = mn;
         }
 #pragma unroll
         for (int e = 0; e < kPer; ++e) red_o[wave][e * 64 + lane] = acc[e];
     } else {
         // lanes over (result, 4 consecutive d): a wave reads 64 / (D / 4)
-        // results per load, 16 bytes per lane, and sums them up the lane bits
-        // above d
+        // results per load, 16 bytes per lane, and combines them up the lane
+        // bits above d
         constexpr int kLanesPerPart = D / 4;
         constexpr int kPartsPerWave = 64 / kLanesPerPart;
         const int sub = lane / kLanesPerPart;
         const int d4 = lane % kLanesPerPart;
         float4 acc = {0.f, 0.f, 0.f, 0.f};
-        if (m != -INFINITY) {
 #pragma unroll 4
-            for (int64_t w = w_lo + wave * kPartsPerWave + sub; w <= w_hi; w += NW * kPartsPerWave) {
-                const int64_t sr = (w + slot0) * p.rslot + rs;
-                const float mc = pml[2 * sr];
-                const float wt = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - m);
-                if (d4 == 0) l += wt * pml[2 * sr + 1];
-                const float4 v = *reinterpret_cast<const float4 *>(p.part + sr * D + 4 * d4);
-                acc.x += wt * v.x;
-                acc.y += wt * v.y;
-                acc.z += wt * v.z;
-                acc.w += wt * v.w;
-            }
+        for (int64_t w = w_lo + wave * kPartsPerWave + sub; w <= w_hi; w += NW * kPartsPerWave) {
+            const int64_t sr = (w + slot0) * p.rslot + rs;
+            const float mc = pml[2 * sr];
+            const float lc = pml[2 * sr + 1];
+            const float4 v = *reinterpret_cast<const float4 *>(p.part + sr * D + 4 * d4);
+            const float mn = fmaxf(m, mc);
+            const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+            const float wt = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - mn);
+            l = alpha * l + wt * lc;
+            acc.x = alpha * acc.x + wt * v.x;
+            acc.y = alpha * acc.y + wt * v.y;
+            acc.z = alpha * acc.z + wt * v.z;
+            acc.w = alpha * acc.w + wt * v.w;
+            m = mn;
         }
 #pragma unroll
         for (int off = kLanesPerPart; off < 64; off *= 2) {
-            acc.x += __shfl_xor(acc.x, off);
-            acc.y += __shfl_xor(acc.y, off);
-            acc.z += __shfl_xor(acc.z, off);
-            acc.w += __shfl_xor(acc.w, off);
-            l += __shfl_xor(l, off);
+            const float mo = __shfl_xor(m, off);
+            const float lo = __shfl_xor(l, off);
+            const float4 ao = {__shfl_xor(acc.x, off), __shfl_xor(acc.y, off), __shfl_xor(acc.z, off),
+                               __shfl_xor(acc.w, off)};
+            const float mn = fmaxf(m, mo);
+            const float a = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+            const float c = mo == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mo - mn);
+            l = a * l + c * lo;
+            acc.x = a * acc.x + c * ao.x;
+            acc.y = a * acc.y + c * ao.y;
+            acc.z = a * acc.z + c * ao.z;
+            acc.w = a * acc.w + c * ao.w;
+            m = mn;
         }
         if (lane < kLanesPerPart) {
             red_o[wave][4 * d4] = acc.x;
@@ -554,20 +564,31 @@ __global__ __launch_bounds__(64 * NW) void attn_decode_merge_kernel(DecParams p)
             red_o[wave][4 * d4 + 3] = acc.w;
         }
     }
-    if (lane == 0) red_o[wave][D] = l;
+    if (lane == 0) {
+        red_m[wave] = m;
+        red_o[wave][D] = l;
+    }
     __syncthreads();
     if (wave != 0) return;
+    float mx = red_m[0];
+#pragma unroll
+    for (int v = 1; v < NW; ++v) mx = fmaxf(mx, red_m[v]);
+    float sc[NW];  // each wave's rescale to the largest maximum
     l = 0.f;
 #pragma unroll
-    for (int v = 0; v < NW; ++v) l += red_o[v][D];
+    for (int v = 0; v < NW; ++v) {
+        sc[v] = red_m[v] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(red_m[v] - mx);
+        l += sc[v] * red_o[v][D];
+    }
+    m = mx;
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    T *orow = static_cast<T *>(p.o) + row * D;
+    T *orow = static_cast<T *>(p.o) + (int64_t)row * D;
 #pragma unroll
     for (int e = 0; e < D / 64; ++e) {
         const int d = e * 64 + lane;
         float o = 0.f;
 #pragma unroll
-        for (int v = 0; v < NW; ++v) o += red_o[v][d];
+        for (int v = 0; v < NW; ++v) o += sc[v] * red_o[v][d];
         orow[d] = (T)(o * inv);
     }
     if (lane == 0) p.lse[row] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;

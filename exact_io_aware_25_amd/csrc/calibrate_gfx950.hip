@@ -29,6 +29,12 @@
 //   calibrate_gfx950 --read    HBM read rate of a plain kernel over 3.3 GB,
 //       the data read in 4 KiB blocks in order and in a random order (the
 //       access pattern of a paged KV cache).
+//   calibrate_gfx950 --atomics fp32 atomic adds as an atomic dQ would issue
+//       them in the backward at causal L = 131072, H = 4, d = 64: one
+//       workgroup per 128-key block and head adds a 64 x 64 fp32 tile into dQ
+//       for every 64-row query tile whose rows see its keys (1.72e10 adds,
+//       no return value); the time, the adds per second, and a check of every
+//       sum.
 //
 // Every memory access stays inside the buffers it is given.
 #include <hip/hip_runtime.h>
@@ -637,6 +643,57 @@ static int run_read()
     return 0;
 }
 
+// ------------------------------------------------------------------ fp32 atomics
+// Workgroup (h, kb) adds 1 to every element of the 64 x 64 tiles qt >= 2 kb
+// of head h; element i of a tile is added by thread i % 256.
+__global__ __launch_bounds__(256) void dq_atomics(float *dq, int n_qtiles, int kblocks)
+{
+    const int kb = blockIdx.x % kblocks;
+    const int h = blockIdx.x / kblocks;
+    float *dqh = dq + (int64_t)h * n_qtiles * 4096;
+    for (int qt = 2 * kb; qt < n_qtiles; ++qt) {
+        float *tile = dqh + (int64_t)qt * 4096;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            __hip_atomic_fetch_add(tile + i * 256 + threadIdx.x, 1.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+static int run_atomics()
+{
+    const int H = 4, n_qtiles = 131072 / 64, kblocks = 131072 / 128;
+    const size_t n = (size_t)H * n_qtiles * 4096;
+    float *dq;
+    CHECK_HIP(hipMalloc(&dq, n * sizeof(float)));
+    double adds = 0;
+    for (int kb = 0; kb < kblocks; ++kb) adds += (double)(n_qtiles - std::min(2 * kb, n_qtiles)) * 4096 * H;
+    std::vector<float> h(n);
+    int bad = 0;
+    for (int rep = 0; rep < 3; ++rep) {
+        CHECK_HIP(hipMemset(dq, 0, n * sizeof(float)));
+        CHECK_HIP(hipDeviceSynchronize());
+        hipEvent_t e0, e1;
+        CHECK_HIP(hipEventCreate(&e0));
+        CHECK_HIP(hipEventCreate(&e1));
+        CHECK_HIP(hipEventRecord(e0));
+        hipLaunchKernelGGL(dq_atomics, dim3(H * kblocks), dim3(256), 0, 0, dq, n_qtiles, kblocks);
+        CHECK_HIP(hipEventRecord(e1));
+        CHECK_HIP(hipEventSynchronize(e1));
+        float ms = 0;
+        CHECK_HIP(hipEventElapsedTime(&ms, e0, e1));
+        CHECK_HIP(hipMemcpy(h.data(), dq, n * sizeof(float), hipMemcpyDeviceToHost));
+        for (size_t i = 0; i < n; ++i) {
+            const int qt = (int)(i / 4096 % n_qtiles);
+            if (h[i] != (float)std::min(qt / 2 + 1, kblocks)) ++bad;
+        }
+        std::printf("fp32 atomic adds, atomic-dQ pattern of causal 128k H=4 d=64: %.3g adds in %.2f ms = %.3g adds/s "
+                    "(%.0f GB/s of fp32 payload)\n", adds, ms, adds / (ms * 1e-3), adds * 4 / (ms * 1e-3) / 1e9);
+    }
+    std::printf("every sum equals the number of key blocks that add to it: %s\n", bad ? "NO" : "yes");
+    CHECK_HIP(hipFree(dq));
+    return bad ? 1 : 0;
+}
+
 int main(int argc, char **argv)
 {
     const char *mode = argc > 1 ? argv[1] : "";
@@ -644,6 +701,7 @@ int main(int argc, char **argv)
     if (std::strcmp(mode, "--rates") == 0) return run_rates();
     if (std::strcmp(mode, "--read") == 0) return run_read();
     if (std::strcmp(mode, "--fp8acc") == 0) return run_fp8acc();
-    std::printf("usage: %s --check | --rates | --read | --fp8acc\n", argv[0]);
+    if (std::strcmp(mode, "--atomics") == 0) return run_atomics();
+    std::printf("usage: %s --check | --rates | --read | --fp8acc | --atomics\n", argv[0]);
     return 2;
 }

@@ -7,8 +7,9 @@ bound derived from the arithmetic (weights rounded to the 16-bit type before
 the product, fp32 sums) to the grid of small ragged batches.  Cases: a grid of small ragged batches
 (several chunks per sequence, more than 32 query rows per K/V head, every
 block size and mask kind), the decode workloads at full size against the
-whole oracle, and invariants (block placement, lengths clamped to
-max_seq_len, sequences shorter than Lq).
+whole oracle, invariants (block placement, lengths clamped to max_seq_len,
+sequences shorter than Lq), and the partial kernel's even split of the tile
+list (more than 64 sequences, empty sequences among them, all empty).
 """
 import numpy as np
 import pytest
@@ -124,3 +125,40 @@ def test_decode_rejects_bad_workspace_and_outputs():
     out, lse = attn.decode(q, kc, vc, bt, sl, 100)  # and the defaults still work
     torch.cuda.synchronize(DEV)
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("case", [(150, 8, 2, 1, 64, "f16", 16), (70, 16, 1, 3, 128, "bf16", 32)],
+                         ids=["B150-H8/2-Lq1-d64-f16", "B70-H16/1-Lq3-d128-bf16"])
+def test_decode_many_sequences_with_empty_ones(case):
+    """More than 64 sequences (the partial kernel's prefix sum over the
+    lengths takes several 64-lane passes), every fifth one empty, the rest of
+    seeded ragged lengths: the waves' equal runs of the tile list cross many
+    sequence (and row-block) boundaries.  Empty sequences give O = 0 and
+    lse = -inf; the others match the oracle within the derived bound."""
+    B, H, H_kv, Lq, d, dtype, bs = case
+    announce(f"decode many sequences {case}")
+    gen = torch.Generator().manual_seed(B + d)
+    lens = torch.randint(Lq, 900, (B,), generator=gen).tolist()
+    for b in range(0, B, 5):
+        lens[b] = 0
+    q, kc, vc, bt, sl = make_paged(B, H, H_kv, d, dtype, Lq, lens, bs, seed=B * 7 + d)
+    scale = 0.125 if d == 64 else None
+    out, lse = gpu_decode(q, kc, vc, bt, sl, max(lens), -1, scale)
+    empty = [b for b in range(B) if lens[b] == 0]
+    live = [b for b in range(B) if lens[b] > 0]
+    assert torch.all(out[empty] == 0) and torch.all(torch.isneginf(lse[empty]))
+    ref = paged.decode_attention(q[live], kc, vc, bt[live], [lens[b] for b in live], dtype, -1,
+                                 0.0 if scale is None else scale, with_abs=True)
+    check(out[live], lse[live], ref, dtype, f"decode many sequences {case}", vmax=float(vc.abs().max()))
+
+
+def test_decode_all_sequences_empty():
+    """No sequence holds a token: no wave of the partial kernel has work, and
+    every row comes out as O = 0, lse = -inf."""
+    B, H, H_kv, Lq, d, bs = 3, 4, 2, 2, 64, 16
+    announce("decode all empty")
+    q, kc, vc, _, _ = make_paged(B, H, H_kv, d, "f16", Lq, [16] * B, bs, seed=4)
+    bt = torch.full((B, 1), -1, dtype=torch.int32)
+    sl = torch.zeros(B, dtype=torch.int32)
+    out, lse = gpu_decode(q, kc, vc, bt, sl, 16, -1, 0.125)
+    assert torch.all(out == 0) and torch.all(torch.isneginf(lse))

@@ -361,9 +361,11 @@ def cpu_baseline(w, out, lse, inputs, budget_s: float = 15.0, seed: int = 7):
         err_l = max(err_l, float(np.abs(gl - rl).max()))
         done += len(rows)
         batch = min(4096, batch * 2)
-    return dict(value=flops / elapsed / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
+    rate = flops / elapsed
+    return dict(value=rate / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
                 sample=f"{done} seeded random query rows of {n_total} ({w.name}), "
                        f"{elapsed:.1f} s of fp64 oracle time, {flops:.3e} algorithmic FLOPs",
+                extrapolated_full_s=round(algorithmic_flops(w) / rate, 1), cpu_model=cpu_model(),
                 parity_max_abs_o=err_o, parity_max_abs_lse=err_l)
 
 

@@ -114,7 +114,6 @@ def time_workload(w, steps: int, warmup: int):
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats(dev)
     base = torch.cuda.memory_allocated(dev)
-    free_before = torch.cuda.mem_get_info(dev)[0]
     out = torch.empty(q.shape, dtype=torch.bfloat16 if w.dtype == "f8" else q.dtype, device=dev)
     lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -122,6 +121,10 @@ def time_workload(w, steps: int, warmup: int):
         attn.forward(q, k, v, causal=w.causal, window=w.window, scale=w.scale, out=out, lse=lse,
                      stream=stream)
     torch.cuda.synchronize()
+    # device memory free, by the driver's count, with the outputs allocated and
+    # the code loaded: the timed calls must not change it (the library
+    # allocates nothing)
+    free_before = torch.cuda.mem_get_info(dev)[0]
     # one event between consecutive launches: the first and last bracket the
     # timed region (its mean is the step time), the others give each launch
     events = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]

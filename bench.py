@@ -606,10 +606,22 @@ def main():
     if args.sweep:
         sweep = []
         for name, ws in WORKLOADS.items():
-            rs = time_workload(ws, max(5, args.steps), 3)
+            # 10 warm-up and 100 timed calls up to 32k tokens, 3 and 20 beyond
+            # (or --steps, if larger)
+            short = ws.L <= 32768
+            steps, warm = max(100 if short else 20, args.steps), 10 if short else 3
+            try:
+                rs = time_workload(ws, steps, warm)
+            except torch.cuda.OutOfMemoryError:
+                rec = {"workload": name, "dtype": ws.dtype, "L": ws.L, "ms": "OOM", "ms_median": "OOM",
+                       "ms_min": "OOM", "tflops": "OOM", "pct_peak": "OOM", "peak_mem_bytes": "OOM"}
+                sweep.append(rec)
+                print(json.dumps(rec), file=sys.stderr, flush=True)
+                torch.cuda.empty_cache()
+                continue
             f = algorithmic_flops(ws)
-            rec = {"workload": name, "dtype": ws.dtype, "L": ws.L, "ms": round(rs["ms"], 4),
-                   "ms_median": round(rs["ms_median"], 4), "ms_min": round(rs["ms_min"], 4),
+            rec = {"workload": name, "dtype": ws.dtype, "L": ws.L, "steps": steps, "warmup": warm,
+                   "ms": round(rs["ms"], 4), "ms_median": round(rs["ms_median"], 4), "ms_min": round(rs["ms_min"], 4),
                    "tflops": round(f / (rs["ms"] * 1e-3) / 1e12, 2),
                    "pct_peak": round(100 * f / (rs["ms"] * 1e-3) / 1e12 / mfma_peak(ws), 2),
                    "peak_mem_bytes": rs["peak_mem"], "peak_mem_call_bytes": rs["peak_mem_call"],
@@ -621,7 +633,7 @@ def main():
         # the pages' length sweep (causal, B=1, H=4, d=64): log-log slopes of time and memory
         pts = sorted((rec["L"], rec["ms"], rec["peak_mem_bytes"]) for rec in sweep
                      if rec["workload"] in ("causal_4k", "causal_8k", "causal_16k", "causal_32k",
-                                            "causal_64k", "causal_128k_h4"))
+                                            "causal_64k", "causal_128k_h4") and rec["ms"] != "OOM")
         Ls, ts, ms_ = zip(*pts)
         print(json.dumps({"length_sweep": {"L": Ls, "ms": ts, "peak_mem_bytes": ms_,
                                            "slope_time": round(loglog_slope(Ls, ts), 3),
@@ -631,7 +643,8 @@ def main():
             write_csv(args.csv, ["workload", "dtype", "L", "time_ms", "time_ms_median", "time_ms_min", "mem_GB",
                                  "tflops", "pct_peak"],
                       [[r["workload"], r["dtype"], r["L"], r["ms"], r["ms_median"], r["ms_min"],
-                        round(r["peak_mem_bytes"] / 1e9, 6), r["tflops"], r["pct_peak"]] for r in sweep])
+                        "OOM" if r["peak_mem_bytes"] == "OOM" else round(r["peak_mem_bytes"] / 1e9, 6),
+                        r["tflops"], r["pct_peak"]] for r in sweep])
 
 
 def standard_attention(q, k, v, causal: bool, scale: float, rows_per_step: int = 8192,

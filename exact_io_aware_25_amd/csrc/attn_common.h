@@ -305,6 +305,115 @@ struct MergeLayout {
     __host__ __device__ static constexpr int slot_float_offset(int i) { return (i % kPerBuffer) * 64 * kPart; }
 };
 
+// ---- paged decode: the list of key tiles that the partial kernel splits into
+// equal runs of P = max(ceil(total / W), kMinTiles) tiles over W waves.
+constexpr int kDecTile = 32;     // keys per tile
+constexpr int kMaxWaves = 4096;  // most waves of the partial kernel (bounds the workspace)
+constexpr int kMinTiles = 8;     // fewest tiles per wave
+
+// Row blocks (of up to 32 query rows of one K/V head), segments per sequence,
+// rows per result slot, and the most waves a call of this shape can use (one
+// wave per kMinTiles tiles of the longest possible list, at most kMaxWaves);
+// each wave writes at most one result per segment it touches, and the runs
+// are consecutive, so waves_cap + B * nseg slots hold them all.  Host side.
+struct DecodeShape {
+    int64_t rows, n_rowblk, nseg, rslot, waves_cap, n_slots;
+};
+inline DecodeShape decode_shape(int64_t B, int64_t H, int64_t H_kv, int64_t Lq, int64_t max_len)
+{
+    DecodeShape s;
+    s.rows = H / H_kv * Lq;
+    s.n_rowblk = (s.rows + 31) / 32;
+    s.nseg = H_kv * s.n_rowblk;
+    s.rslot = s.rows < 32 ? s.rows : 32;
+    const int64_t tiles = B * s.nseg * ((max_len + kDecTile - 1) / kDecTile);
+    const int64_t cap = (tiles + kMinTiles - 1) / kMinTiles;
+    s.waves_cap = cap < 1 ? 1 : (cap > kMaxWaves ? kMaxWaves : cap);
+    s.n_slots = s.waves_cap + B * s.nseg;
+    return s;
+}
+
+// A sequence of n tokens (n already clamped) whose last Lq tokens are the
+// query rows: the first key one of them sees, and the 32-key tiles
+// [t_lo, t_hi) holding every such key (none when n = 0).
+__host__ __device__ __forceinline__ int decode_first_key(int n, int Lq, int window)
+{
+    return window >= 0 && n - Lq - window > 0 ? n - Lq - window : 0;
+}
+struct DecSeqTiles {
+    int t_lo, t_hi;
+};
+__host__ __device__ __forceinline__ DecSeqTiles decode_seq_tiles(int n, int Lq, int window)
+{
+    DecSeqTiles st;
+    st.t_lo = decode_first_key(n, Lq, window) / kDecTile;
+    st.t_hi = (n + kDecTile - 1) / kDecTile;
+    return st;
+}
+
+// A position in the tile list: sequence b (n tokens, tiles [t_lo, t_hi)),
+// K/V head g, row block rb, tile t.  The list runs over t, then rb, then g,
+// then the sequences that have tiles.
+struct DecCursor {
+    int b, g, rb, t, t_lo, t_hi, n;
+};
+
+// The cursor at tile `off` (< tiles * H_kv * n_rowblk) of sequence b's part
+// of the list.
+__host__ __device__ __forceinline__ DecCursor decode_cursor_at(int b, int n, DecSeqTiles st, int64_t off,
+                                                               int n_rowblk)
+{
+    DecCursor c;
+    c.b = b;
+    c.n = n;
+    c.t_lo = st.t_lo;
+    c.t_hi = st.t_hi;
+    const int tiles = st.t_hi - st.t_lo;
+    const int seg = (int)(off / tiles);
+    c.t = st.t_lo + (int)(off % tiles);
+    c.g = seg / n_rowblk;
+    c.rb = seg % n_rowblk;
+    return c;
+}
+
+// The tile after c; len(b) is sequence b's clamped length.  Sequences without
+// tiles are skipped; past the last tile of the list the cursor stays inside
+// the last sequence (a valid tile, not part of any run).
+template <typename LenFn>
+__host__ __device__ __forceinline__ DecCursor decode_next_tile(DecCursor c, int B, int H_kv, int n_rowblk, int Lq,
+                                                               int window, LenFn len)
+{
+    if (++c.t < c.t_hi) return c;
+    c.t = c.t_lo;
+    if (++c.rb < n_rowblk) return c;
+    c.rb = 0;
+    if (++c.g < H_kv) return c;
+    c.g = 0;
+    while (c.b + 1 < B) {
+        ++c.b;
+        c.n = len(c.b);
+        const DecSeqTiles st = decode_seq_tiles(c.n, Lq, window);
+        c.t_lo = st.t_lo;
+        c.t_hi = st.t_hi;
+        if (c.t_hi > c.t_lo) break;
+    }
+    c.t = c.t_lo;
+    return c;
+}
+
+// The waves whose runs of P consecutive tiles meet a segment of `tiles`
+// tiles (> 0) that starts at list position f_seg: w_lo .. w_hi.
+struct DecWaves {
+    int64_t lo, hi;
+};
+__host__ __device__ __forceinline__ DecWaves decode_segment_waves(int64_t f_seg, int64_t tiles, int64_t P)
+{
+    DecWaves w;
+    w.lo = f_seg / P;
+    w.hi = (f_seg + tiles - 1) / P;
+    return w;
+}
+
 // Do the byte ranges [a, a+na) and [b, b+nb) overlap?
 inline bool overlaps(const void *a, size_t na, const void *b, size_t nb)
 {

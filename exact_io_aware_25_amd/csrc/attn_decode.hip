@@ -43,10 +43,7 @@
 
 namespace {
 
-constexpr int kDecTile = 32;     // keys per tile
-constexpr int kDecWaves = 4;     // independent waves per workgroup
-constexpr int kMaxWaves = 4096;  // most waves of the partial kernel (bounds the workspace)
-constexpr int kMinTiles = 8;     // fewest tiles per wave
+constexpr int kDecWaves = 4;     // independent waves per workgroup (tiles: kDecTile keys)
 constexpr int kMaxDevices = 64;
 constexpr float kLn2 = 0.69314718055994531f;
 
@@ -79,12 +76,6 @@ __device__ __forceinline__ int seq_len(const DecParams &p, int b)
     return min(max(load_invariant(p.lens + b), 0), p.max_len);
 }
 
-// First key any query row of a sequence of n tokens can see.
-__device__ __forceinline__ int first_key(const DecParams &p, int n)
-{
-    return p.window >= 0 ? max(0, n - p.Lq - p.window) : 0;
-}
-
 // Page-table entry for key j of sequence b (the logical block number is
 // clamped), and the physical block it names (the entry is clamped too, so a
 // bad table reads a wrong block, never out of bounds).
@@ -99,44 +90,17 @@ __device__ __forceinline__ int64_t physical_block(const DecParams &p, int entry)
     return min(max(entry, 0), p.num_blocks - 1);
 }
 
-// A position in the tile list: sequence b (n tokens, tiles [t_lo, t_hi) hold
-// every key one of its query rows can see), K/V head g, row block rb, tile t.
-struct Cursor {
-    int b, g, rb, t, t_lo, t_hi, n;
-};
-
-__device__ __forceinline__ void set_sequence(const DecParams &p, Cursor &c, int b)
-{
-    c.b = b;
-    c.n = seq_len(p, b);
-    c.t_lo = first_key(p, c.n) / kDecTile;
-    c.t_hi = (c.n + kDecTile - 1) / kDecTile;  // n = 0: no tile
-}
-
 // Tiles of sequence b over all its segments.
 __device__ __forceinline__ int64_t sequence_span(const DecParams &p, int b)
 {
-    Cursor c;
-    set_sequence(p, c, b);
-    return (int64_t)(c.t_hi - c.t_lo) * p.nseg;
+    const DecSeqTiles st = decode_seq_tiles(seq_len(p, b), p.Lq, p.window);
+    return (int64_t)(st.t_hi - st.t_lo) * p.nseg;
 }
 
-// The tile after c (sequences without tiles are skipped; past the last tile
-// of the list the cursor stays inside the last sequence and is not used).
-__device__ __forceinline__ Cursor next_tile(const DecParams &p, Cursor c)
+// The tile after c (see decode_next_tile).
+__device__ __forceinline__ DecCursor next_tile(const DecParams &p, DecCursor c)
 {
-    if (++c.t < c.t_hi) return c;
-    c.t = c.t_lo;
-    if (++c.rb < p.n_rowblk) return c;
-    c.rb = 0;
-    if (++c.g < p.H_kv) return c;
-    c.g = 0;
-    while (c.b + 1 < p.B) {
-        set_sequence(p, c, c.b + 1);
-        if (c.t_hi > c.t_lo) break;
-    }
-    c.t = c.t_lo;
-    return c;
+    return decode_next_tile(c, p.B, p.H_kv, p.n_rowblk, p.Lq, p.window, [&](int b) { return seq_len(p, b); });
 }
 
 __device__ __forceinline__ int64_t uniform64(int64_t x)
@@ -214,7 +178,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void attn_decode_partial_kernel(Dec
     if (f_begin >= f_end) return;
 
     // ---- the cursor at f_begin: the sequence whose tiles hold it, then segment and tile
-    Cursor c0;
+    DecCursor c0;
     {
         int64_t run = 0;
         for (int b0 = 0; b0 < p.B; b0 += 64) {
@@ -225,12 +189,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void attn_decode_partial_kernel(Dec
             if (found) {
                 const int l = __builtin_ctzll(found);
                 const int64_t off = f_begin - run - uniform64(__shfl((long long)(incl - span), l));
-                set_sequence(p, c0, b0 + l);
-                const int tiles = c0.t_hi - c0.t_lo;  // > 0: the sequence holds f_begin
-                const int seg = (int)(off / tiles);
-                c0.t = c0.t_lo + (int)(off % tiles);
-                c0.g = seg / p.n_rowblk;
-                c0.rb = seg % p.n_rowblk;
+                const int n = seq_len(p, b0 + l);  // the sequence holds f_begin, so it has tiles
+                c0 = decode_cursor_at(b0 + l, n, decode_seq_tiles(n, p.Lq, p.window), off, p.n_rowblk);
                 break;
             }
             run += uniform64(__shfl((long long)incl, 63));
@@ -253,21 +213,21 @@ __global__ __launch_bounds__(64 * kDecWaves) void attn_decode_partial_kernel(Dec
     // scalar loads).  They are fetched two tiles ahead and clamped only where
     // used, so a tile's data loads never wait on a page-table load.
     struct Pages { int lo, hi; };
-    auto pages_of = [&](const Cursor &c) {
+    auto pages_of = [&](const DecCursor &c) {
         Pages pg;
         pg.lo = table_entry(p, c.b, c.t * kDecTile);
         pg.hi = table_entry(p, c.b, c.t * kDecTile + 16);
         return pg;
     };
     // K fragments of a tile into registers; its V tile into this wave's stage
-    auto load_k = [&](const Cursor &c, Pages pg, vec8 (&kf)[kDSteps]) {
+    auto load_k = [&](const DecCursor &c, Pages pg, vec8 (&kf)[kDSteps]) {
         const int j = c.t * kDecTile + krow;  // krow < 16 exactly when l32 < 16
         const int64_t page = physical_block(p, l32 < 16 ? pg.lo : pg.hi);
         const T *row = kc + ((page * p.H_kv + c.g) * p.bs + (j & (p.bs - 1))) * D;
 #pragma unroll
         for (int s = 0; s < kDSteps; ++s) kf[s] = *reinterpret_cast<const vec8 *>(row + 16 * s + 8 * hi);
     };
-    auto copy_v = [&](const Cursor &c, Pages pg, char *stage) {
+    auto copy_v = [&](const DecCursor &c, Pages pg, char *stage) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             const int j0 = c.t * kDecTile + 16 * hf;
@@ -313,7 +273,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void attn_decode_partial_kernel(Dec
         }
     };
     // start accumulating the segment of cursor c
-    auto begin_segment = [&](const Cursor &c) {
+    auto begin_segment = [&](const DecCursor &c) {
         seg_b = c.b;
         seg_g = c.g;
         seg_rb = c.rb;
@@ -323,7 +283,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void attn_decode_partial_kernel(Dec
         const int qi = row_live ? r % p.Lq : 0;
         const int h = c.g * p.group + hh;
         pos = c.n - p.Lq + qi;  // its position (rows with pos < 0 see no key)
-        k_begin = first_key(p, c.n);
+        k_begin = decode_first_key(c.n, p.Lq, p.window);
         k_end = c.n;
         max_pos = c.n - 1;
         min_pos = c.n - p.Lq;
@@ -343,7 +303,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void attn_decode_partial_kernel(Dec
         l_run = 0.f;
     };
 
-    auto process = [&](const Cursor &c, const vec8 (&kf)[kDSteps], const char *tv) {
+    auto process = [&](const DecCursor &c, const vec8 (&kf)[kDSteps], const char *tv) {
         if (c.b != seg_b || c.g != seg_g || c.rb != seg_rb) {
             if (seg_b >= 0) flush();
             begin_segment(c);
@@ -414,8 +374,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void attn_decode_partial_kernel(Dec
     char *stage_a = lds_a[wave];
     char *stage_b = lds_b[wave];
     vec8 kf_a[kDSteps], kf_b[kDSteps];
-    Cursor c1 = next_tile(p, c0);  // past the end of the run: a tile inside the list, not processed
-    Cursor c2 = next_tile(p, c1);
+    DecCursor c1 = next_tile(p, c0);  // past the end of the run: a tile inside the list, not processed
+    DecCursor c2 = next_tile(p, c1);
     Pages pg0 = pages_of(c0);
     Pages pg1 = pages_of(c1);
     load_k(c0, pg0, kf_a);
@@ -432,7 +392,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void attn_decode_partial_kernel(Dec
         if (!has1) break;
 
         const bool has2 = f + 2 < f_end;
-        const Cursor c3 = next_tile(p, c2);
+        const DecCursor c3 = next_tile(p, c2);
         __builtin_amdgcn_s_waitcnt(0xC07F);
         load_k(has2 ? c2 : c1, has2 ? pg2 : pg1, kf_a);
         copy_v(has2 ? c2 : c1, has2 ? pg2 : pg1, stage_a);
@@ -477,12 +437,9 @@ __global__ __launch_bounds__(64 * NW) void attn_decode_merge_kernel(DecParams p)
     const int64_t seq_first = p.hdr[b];
     const int64_t tiles = (p.hdr[b + 1] - seq_first) / p.nseg;  // tiles of each segment of sequence b
     const int64_t P = p.hdr[p.B + 1];
-    int64_t w_lo = 0, w_hi = -1;  // none when the sequence has no tile
-    if (tiles > 0) {
-        const int64_t f_seg = seq_first + seg * tiles;
-        w_lo = f_seg / P;
-        w_hi = (f_seg + tiles - 1) / P;
-    }
+    DecWaves ws = {0, -1};  // none when the sequence has no tile
+    if (tiles > 0) ws = decode_segment_waves(seq_first + seg * tiles, tiles, P);
+    const int64_t w_lo = ws.lo, w_hi = ws.hi;
     const int64_t slot0 = (int64_t)b * p.nseg + seg;  // wave w's result for this segment: slot w + slot0
     const int64_t rs = r % 32;
     const float *pml = p.part + (int64_t)p.n_slots * p.rslot * D;
@@ -595,27 +552,6 @@ __global__ __launch_bounds__(64 * NW) void attn_decode_merge_kernel(DecParams p)
 }
 
 // ------------------------------------------------------------------ host side
-
-struct DecodeShape {
-    int64_t rows, n_rowblk, nseg, rslot, waves_cap, n_slots;
-};
-
-// Row blocks, segments and the most waves a call of this shape can use (one
-// wave per kMinTiles tiles of the longest possible list, at most kMaxWaves);
-// each wave writes at most one result per segment it touches, and the runs
-// are consecutive, so waves_cap + B * nseg slots hold them all.
-DecodeShape decode_shape(int64_t B, int64_t H, int64_t H_kv, int64_t Lq, int64_t max_len)
-{
-    DecodeShape s;
-    s.rows = H / H_kv * Lq;
-    s.n_rowblk = (s.rows + 31) / 32;
-    s.nseg = H_kv * s.n_rowblk;
-    s.rslot = std::min<int64_t>(s.rows, 32);
-    const int64_t tiles = B * s.nseg * ((max_len + kDecTile - 1) / kDecTile);
-    s.waves_cap = std::max<int64_t>(1, std::min<int64_t>(kMaxWaves, (tiles + kMinTiles - 1) / kMinTiles));
-    s.n_slots = s.waves_cap + B * s.nseg;
-    return s;
-}
 
 size_t decode_hdr_bytes(int64_t B)
 {

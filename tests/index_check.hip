@@ -22,7 +22,17 @@
 //     every tile holding a visible (query, key) pair of a wave is processed
 //     and not skipped, tiles marked full hold only visible pairs, skipped
 //     tiles none;
-//   * the merge slots of the split shapes fit their LDS buffers.
+//   * the merge slots of the split shapes fit their LDS buffers;
+//   * the paged decode's even split of its tile list over W waves, for
+//     seeded random batches (empty, short and clamped sequences, windows,
+//     several row blocks, more than 64 sequences): each sequence's tiles hold
+//     every key its query rows see; every wave's run, walked with the
+//     kernel's own cursor steps from the kernel's own starting cursor, visits
+//     list positions f_begin .. f_end - 1 in order (so the runs cover the
+//     list exactly once), inside the sequences, heads and row blocks; every
+//     result slot a wave writes lies below the slot count the workspace
+//     holds; and the merge's wave range of each segment is exactly the set
+//     of waves that wrote a result for it.
 // Exit status 0 when every check holds; the first failures are printed.
 #include <cstdio>
 #include <cstdlib>
@@ -415,6 +425,110 @@ static void check_merge()
     CHECK(ML::kBatch <= 2 * ML::kPerBuffer, "merge batch larger than the slots");
 }
 
+// ---------------------------------------------------------------- paged decode partition
+static uint64_t g_lcg = 12345;
+static int rnd(int n)  // uniform in [0, n)
+{
+    g_lcg = g_lcg * 6364136223846793005ULL + 1442695040888963407ULL;
+    return (int)((g_lcg >> 33) % (uint64_t)n);
+}
+
+static void check_decode_case(int B, int H_kv, int group, int Lq, int window, int max_len, int W_req,
+                              const std::vector<int> &lens_raw)
+{
+    const DecodeShape sh = decode_shape(B, (int64_t)H_kv * group, H_kv, Lq, max_len);
+    const int n_rowblk = (int)sh.n_rowblk, nseg = (int)sh.nseg;
+    const int W = W_req < sh.waves_cap ? W_req : (int)sh.waves_cap;  // the launch takes min(resident, cap)
+    auto len = [&](int b) {
+        const int n = lens_raw[b] < 0 ? 0 : lens_raw[b];
+        return n < max_len ? n : max_len;
+    };
+    std::vector<int64_t> first(B + 1, 0);
+    std::vector<DecSeqTiles> st(B);
+    for (int b = 0; b < B; ++b) {
+        const int n = len(b);
+        st[b] = decode_seq_tiles(n, Lq, window);
+        CHECK(st[b].t_lo >= 0 && st[b].t_hi >= st[b].t_lo, "decode: sequence %d tiles [%d, %d)", b, st[b].t_lo, st[b].t_hi);
+        // every key a query row of the sequence sees lies in its tiles
+        for (int i = 0; i < Lq; ++i) {
+            const int pos = n - Lq + i;
+            if (pos < 0) continue;
+            const int lo = window >= 0 && pos - window > 0 ? pos - window : 0;
+            CHECK(lo >= kDecTile * st[b].t_lo && pos < kDecTile * st[b].t_hi,
+                  "decode: n=%d Lq=%d window=%d row %d sees keys %d..%d outside tiles [%d, %d)", n, Lq, window, i, lo,
+                  pos, st[b].t_lo, st[b].t_hi);
+        }
+        first[b + 1] = first[b] + (int64_t)(st[b].t_hi - st[b].t_lo) * nseg;
+    }
+    const int64_t total = first[B];
+    int64_t P = (total + W - 1) / W;
+    if (P < kMinTiles) P = kMinTiles;
+    // segment index (b, g, rb) -> the waves that wrote a result for it
+    std::vector<int64_t> seg_lo((size_t)B * nseg, -1), seg_hi((size_t)B * nseg, -1);
+    for (int w = 0; w < W; ++w) {
+        const int64_t f0 = (int64_t)w * P, f1 = f0 + P < total ? f0 + P : total;
+        if (f0 >= f1) continue;
+        int b = 0;
+        while (first[b + 1] <= f0) ++b;  // the sequence whose tiles hold f0
+        DecCursor c = decode_cursor_at(b, len(b), st[b], f0 - first[b], n_rowblk);
+        int last_seg = -1;
+        for (int64_t f = f0; f < f1; ++f) {
+            const bool inside = c.b >= 0 && c.b < B && c.g >= 0 && c.g < H_kv && c.rb >= 0 && c.rb < n_rowblk &&
+                                c.t >= c.t_lo && c.t < c.t_hi;
+            CHECK(inside, "decode: wave %d at f=%lld: cursor b=%d g=%d rb=%d t=%d [%d, %d) out of range", w,
+                  (long long)f, c.b, c.g, c.rb, c.t, c.t_lo, c.t_hi);
+            if (!inside) return;
+            const int64_t pos = first[c.b] + (int64_t)(c.g * n_rowblk + c.rb) * (c.t_hi - c.t_lo) + (c.t - c.t_lo);
+            CHECK(pos == f, "decode: wave %d step f=%lld is at list position %lld", w, (long long)f, (long long)pos);
+            CHECK(c.t_lo == st[c.b].t_lo && c.t_hi == st[c.b].t_hi && c.n == len(c.b), "decode: cursor tiles stale");
+            const int seg = (c.b * H_kv + c.g) * n_rowblk + c.rb;
+            if (seg != last_seg) {
+                const int64_t slot = (int64_t)w + seg;
+                CHECK(slot < sh.n_slots, "decode: slot %lld of %lld", (long long)slot, (long long)sh.n_slots);
+                if (seg_lo[seg] < 0) seg_lo[seg] = w;
+                CHECK(seg_hi[seg] < w, "decode: wave %d writes segment %d twice or out of order", w, seg);
+                seg_hi[seg] = w;
+                last_seg = seg;
+            }
+            c = decode_next_tile(c, B, H_kv, n_rowblk, Lq, window, len);
+        }
+        // past the end of the run the cursor stays inside the batch (its tile is
+        // loaded but not used)
+        CHECK(c.b >= 0 && c.b < B && c.t >= 0, "decode: cursor past the run leaves the batch");
+    }
+    for (int b = 0; b < B; ++b)
+        for (int sg = 0; sg < nseg; ++sg) {
+            const int seg = b * nseg + sg;
+            const int64_t tiles = st[b].t_hi - st[b].t_lo;
+            if (tiles == 0) {
+                CHECK(seg_lo[seg] < 0, "decode: empty segment %d has results", seg);
+                continue;
+            }
+            const DecWaves ws = decode_segment_waves(first[b] + (int64_t)sg * tiles, tiles, P);
+            CHECK(ws.lo == seg_lo[seg] && ws.hi == seg_hi[seg] && ws.hi < W,
+                  "decode: segment %d: merge reads waves %lld..%lld, written by %lld..%lld (W=%d)", seg,
+                  (long long)ws.lo, (long long)ws.hi, (long long)seg_lo[seg], (long long)seg_hi[seg], W);
+        }
+}
+
+static void check_decode_partition()
+{
+    const int windows[] = {-1, -1, 0, 5, 100, 4096};
+    const int waves[] = {1, 3, 64, 2048, 3072, 4096};
+    for (int trial = 0; trial < 400; ++trial) {
+        const int B = 1 + rnd(trial % 4 == 0 ? 150 : 12);
+        const int H_kv = 1 + rnd(4), group = 1 + rnd(12), Lq = 1 + rnd(5);
+        const int window = windows[rnd(6)];
+        const int max_len = 1 + rnd(trial % 3 == 0 ? 20000 : 3000);
+        std::vector<int> lens(B);
+        for (int b = 0; b < B; ++b) {
+            const int kind = rnd(6);
+            lens[b] = kind == 0 ? 0 : kind == 1 ? -5 : kind == 2 ? max_len + 100 : kind == 3 ? 1 : rnd(max_len + 1);
+        }
+        check_decode_case(B, H_kv, group, Lq, window, max_len, waves[rnd(6)], lens);
+    }
+}
+
 int main()
 {
     check_operand_layout();
@@ -438,6 +552,7 @@ int main()
     check_merge<128, 4, 2>();
     check_merge<64, 4, 4>();
     check_merge<64, 2, 4>();
+    check_decode_partition();
     std::printf("%s (%d failures)\n", g_failures ? "INDEX CHECKS FAILED" : "all index checks passed", g_failures);
     return g_failures ? 1 : 0;
 }

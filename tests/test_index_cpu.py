@@ -3,8 +3,10 @@ of the tile copies and fragment reads (16-bit forward, backward, fp8
 forward, paged decode) lies inside its tile and delivers the element the
 MFMA operand layout needs, the swizzles are bijections, the key-tile ranges
 and skip/full/edge classes are right for every launch shape, mask and a set
-of ragged lengths, and the merge slots fit (tests/index_check.hip, built
-with hipcc as a host program from the kernels' own header).  Planted
+of ragged lengths, the merge slots fit, and the paged decode's even split of
+its tile list visits every tile once and merges exactly the waves that
+wrote (tests/index_check.hip, built with hipcc as a host program from the
+kernels' own header).  Planted
 mistakes in a copy of the header must make it fail."""
 import os
 import shutil
@@ -52,6 +54,12 @@ MUTANTS = {
     "window_skip_off_by_one": ("skip = skip || j_last < qa - window;", "skip = skip || j_last <= qa - window;"),
     "f8_v_row_half": ("const int row = 8 * (grp / 2) + li / 2;", "const int row = 8 * (grp % 2) + li / 2;"),
     "merge_slot_stride": ("return (i % kPerBuffer) * 64 * kPart; }", "return (i % kPerBuffer) * 32 * kPart; }"),
+    "decode_tiles_end_rounds_down": ("st.t_hi = (n + kDecTile - 1) / kDecTile;", "st.t_hi = n / kDecTile;"),
+    "decode_first_key_without_lq": ("return window >= 0 && n - Lq - window > 0 ? n - Lq - window : 0;",
+                                    "return window >= 0 && n - window > 0 ? n - window : 0;"),
+    "decode_row_block_wrap": ("if (++c.rb < n_rowblk) return c;", "if (++c.rb <= n_rowblk) return c;"),
+    "decode_cursor_head_from_wrong_digit": ("c.g = seg / n_rowblk;", "c.g = seg % n_rowblk;"),
+    "decode_merge_one_wave_too_many": ("w.hi = (f_seg + tiles - 1) / P;", "w.hi = (f_seg + tiles) / P;"),
 }
 
 

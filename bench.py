@@ -22,6 +22,8 @@ matrix materialised: matmul, scale, mask, softmax, matmul, in PyTorch on the
 GPU) over the pages' length sweep, with peak memory measured as the pages
 do and out-of-memory recorded rather than fatal; one JSON line per length
 and one summary line (speed-up and memory ratio against the pages' claims).
+PyTorch's own fused attention (scaled_dot_product_attention restricted to its
+FlashAttention backend) is timed beside both, as a same-machine reference.
 
 With --backward, one step is one attn_bwd call (dq, dk, dv for an upstream
 gradient, from the forward's out and lse) on the same workload, and the line
@@ -722,6 +724,20 @@ def compare_one(B, H, L, d, causal, scale, seed, reps=3):
 
     t_f, m_f, o_f = measure(lambda: attn.forward(q, k, v, causal=causal, scale=scale)[0])
     res.update(flash_ms=round(t_f, 4), flash_peak_bytes=m_f)
+    # PyTorch's own fused attention (its FlashAttention backend, precompiled
+    # for this GPU), timed the same way: a same-machine point of comparison
+    # for the kernel, not part of the pages' claims.
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    try:
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            t_l, m_l, o_l = measure(lambda: torch.nn.functional.scaled_dot_product_attention(
+                q, k, v, is_causal=causal, scale=scale))
+        res.update(torch_flash_ms=round(t_l, 4), torch_flash_peak_bytes=m_l,
+                   torch_flash_max_abs_diff=float((o_l.float() - o_f.float()).abs().max()),
+                   kernel_over_torch_flash=round(t_l / t_f, 2))
+        del o_l
+    except RuntimeError as e:  # backend not built for this GPU or shape
+        res.update(torch_flash_ms=None, torch_flash_error=str(e).splitlines()[0][:200])
     try:
         t_s, m_s, o_s = measure(lambda: standard_attention(q, k, v, causal, scale))
         diff = float((o_s.float() - o_f.float()).abs().max())
@@ -752,16 +768,20 @@ def main_compare(args):
             v = r.get(key)
             return "OOM" if r.get("standard_peak_bytes") == "OOM" else (round(v / scale, 6) if v is not None else "")
         write_csv(args.csv, ["B", "H", "L", "d", "causal", "time_ms", "mem_GB", "standard_time_ms",
-                             "standard_mem_GB", "speedup", "memory_ratio"],
+                             "standard_mem_GB", "speedup", "memory_ratio", "torch_flash_time_ms"],
                   [[r["B"], r["H"], r["L"], r["d"], int(r["causal"]), r["flash_ms"],
                     round(r["flash_peak_bytes"] / 1e9, 6), std(r, "standard_ms"),
-                    std(r, "standard_peak_bytes", 1e9), r.get("speedup", ""), r.get("memory_ratio", "")]
+                    std(r, "standard_peak_bytes", 1e9), r.get("speedup", ""), r.get("memory_ratio", ""),
+                    r.get("torch_flash_ms") or ""]
                    for r in rows])
     ok = [r for r in rows if r.get("standard_ms") and r.get("standard_result_valid")]
+    lib = [r for r in rows if r.get("torch_flash_ms")]
     print(json.dumps({"compare_summary": {
         "speedup_range": [min(r["speedup"] for r in ok), max(r["speedup"] for r in ok)],
         "memory_ratio_range": [min(r["memory_ratio"] for r in ok), max(r["memory_ratio"] for r in ok)],
         "standard_oom_at": [r["L"] for r in rows if r.get("standard_peak_bytes") == "OOM"],
+        "kernel_over_torch_flash_range": [min(r["kernel_over_torch_flash"] for r in lib),
+                                          max(r["kernel_over_torch_flash"] for r in lib)] if lib else None,
         "claims": "2-4x faster (more at longer sequences), 10-20x less memory, standard attention OOM at 128k",
     }}), flush=True)
 

@@ -538,6 +538,9 @@ def main():
                          "'OOM' where standard attention ran out of memory) to this CSV file")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (attn_bwd) on the workload instead of the forward")
+    ap.add_argument("--torch-flash", action="store_true",
+                    help="also time PyTorch's fused attention (FlashAttention backend) on the same inputs, "
+                         "forward or backward; one JSON line to stderr")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, run one plain device copy of this many MiB (a reference "
                          "kernel of known traffic for scaling profiler byte counters)")
@@ -599,6 +602,8 @@ def main():
 
     if args.data_sensitivity:
         data_sensitivity(w, r["inputs"], max(5, args.steps))
+    if args.torch_flash and w.dtype in ("f16", "bf16"):
+        torch_flash(w, r["inputs"], args.steps, args.warmup, False, r["ms"])
 
     r = line = None  # the headline's tensors are no longer needed
     torch.cuda.empty_cache()
@@ -753,6 +758,55 @@ def compare_one(B, H, L, d, causal, scale, seed, reps=3):
     return res
 
 
+def torch_flash(w, inputs, steps: int, warmup: int, backward: bool, ms_kernel: float):
+    """PyTorch's own fused attention on the same inputs: scaled_dot_product_attention
+    restricted to its FlashAttention backend (precompiled for this GPU), the
+    forward call, or the backward alone (autograd over a retained forward
+    graph), timed with HIP events like the kernel.  A same-machine point of
+    comparison only; one JSON line to stderr.  Windows have no counterpart
+    there, and a grouped K/V layout is passed as enable_gqa."""
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    rec = {"torch_flash": w.name, "pass": "backward" if backward else "forward", "torch": torch.__version__}
+    if w.window >= 0:
+        rec["error"] = "no sliding-window form in scaled_dot_product_attention"
+        print(json.dumps(rec), file=sys.stderr, flush=True)
+        return rec
+    q, k, v = (t.detach().requires_grad_(backward) for t in inputs[:3])
+    kw = dict(is_causal=w.causal, scale=w.scale, enable_gqa=w.H_kv != w.H)
+    try:
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            if backward:
+                out = torch.nn.functional.scaled_dot_product_attention(q, k, v, **kw)
+                g = inputs[3]
+
+                def step():
+                    return torch.autograd.grad(out, (q, k, v), g, retain_graph=True)
+            else:
+                def step():
+                    return torch.nn.functional.scaled_dot_product_attention(q, k, v, **kw)
+            for _ in range(warmup):
+                res = step()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                res = step()
+            e1.record()
+            torch.cuda.synchronize()
+    except RuntimeError as e:  # backend not built for this GPU, shape or dtype
+        rec["error"] = str(e).splitlines()[0][:200]
+        print(json.dumps(rec), file=sys.stderr, flush=True)
+        return rec
+    ms = e0.elapsed_time(e1) / steps
+    flops = algorithmic_flops_bwd(w) if backward else algorithmic_flops(w)
+    tf = flops / (ms * 1e-3) / 1e12
+    rec.update(ms=round(ms, 4), tflops=round(tf, 1), pct_of_mfma_peak=round(100 * tf / MFMA_PEAK_F16_TFLOPS, 2),
+               kernel_speedup=round(ms / ms_kernel, 2))
+    del res
+    print(json.dumps(rec), file=sys.stderr, flush=True)
+    return rec
+
+
 def main_compare(args):
     """The pages' sweep (causal, B=1, H=4, d=64, fp16, 512 ... 128k) and the
     speed-check shape (B=2, H=8, L=2048, d=64, no mask)."""
@@ -854,6 +908,8 @@ def main_backward(w, args):
     print(json.dumps(line), flush=True)
     if args.data_sensitivity:
         data_sensitivity_bwd(w, r["inputs"], max(3, args.steps // 4))
+    if args.torch_flash:
+        torch_flash(w, r["inputs"], args.steps, args.warmup, True, r["ms"])
 
 
 def data_sensitivity_bwd(w, inputs, steps: int):

@@ -388,7 +388,9 @@ static int time_mfma_random(int waves_per_simd, int cus, float *out, long long *
 
 // ------------------------------------------------------------------ single instructions
 // OP 0: v_exp_f32; 1: v_fma_f32; 2: v_cvt_pk_f16_f32; 3: v_dot2c_f32_f16;
-// 4: 4 MFMA 32x32x16 f16 with 16 independent v_fma_f32 between them.
+// 4: 4 MFMA 32x32x16 f16 with 16 independent v_fma_f32 between them;
+// 5: v_exp_f16 on the low half, then its SDWA form on the high half of the
+// same register, keeping the other half (a pair of fp16 weights in place).
 // 8 independent dependency chains per wave; each iteration issues 8 of the
 // instruction (OP 4: 4 MFMAs and 16 FMAs).  Registers only.
 template <int OP>
@@ -421,6 +423,10 @@ __global__ void op_rate(float *out, int iters, long long *cycles)
                     x[i] = __builtin_bit_cast(float, h);
                 }
                 if (OP == 3) x[i] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x[(i + 1) % 8]), one, x[i], false);
+                if (OP == 5)
+                    asm volatile("v_exp_f16 %0, %0\n\t"
+                                 "v_exp_f16_sdwa %0, %0 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:WORD_1"
+                                 : "+v"(x[i]));
             }
         }
     }
@@ -447,7 +453,7 @@ static int time_op(const char *name, int waves_per_simd, int cus, float *out, lo
     CHECK_HIP(hipMemcpy(c.data(), cyc, sizeof(long long) * n, hipMemcpyDeviceToHost));
     long long slowest = 0;
     for (long long v : c) slowest = v > slowest ? v : slowest;
-    const double per_wave = (double)slowest / iters / (OP == 4 ? 1 : 8);
+    const double per_wave = (double)slowest / iters / (OP == 4 ? 1 : OP == 5 ? 16 : 8);
     std::printf("%-44s waves/SIMD %d  %7.2f clocks per %s per wave (slowest wave), %6.2f per SIMD\n", name,
                 waves_per_simd, per_wave, OP == 4 ? "iteration" : "instruction", per_wave / waves_per_simd);
     return 0;
@@ -478,6 +484,7 @@ static int run_rates()
         rc |= time_op<1>("v_fma_f32", w, cus, out, cyc);
         rc |= time_op<2>("v_cvt_pk_f16_f32", w, cus, out, cyc);
         rc |= time_op<3>("v_dot2c_f32_f16", w, cus, out, cyc);
+        rc |= time_op<5>("v_exp_f16 (low half, then SDWA high half)", w, cus, out, cyc);
     }
     rc |= time_op<4>("4 MFMA (128 clocks) + 16 independent fma", 1, cus, out, cyc);
     CHECK_HIP(hipFree(out));

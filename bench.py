@@ -147,6 +147,98 @@ def time_workload(w, steps: int, warmup: int):
                 peak_mem_call=peak - base, device_free_delta=free_before - free_after)
 
 
+def input_cases(q, k, v):
+    """The seeded N(0,1) inputs and three variants with the same shape and
+    fewer significant bits: rounded to 8 bits (held in the input type),
+    signed powers of two, zeros."""
+    dt = q.dtype
+
+    def fewer_bits(t):  # bf16 and fp8 values have 8 or fewer significant bits already
+        return t.to(torch.bfloat16).to(dt) if dt == torch.float16 else t
+
+    def pow2(t):
+        f = t.float()
+        return (torch.sign(f) * torch.exp2(torch.round(torch.log2(f.abs().clamp(min=2.0 ** -14))))).to(dt)
+
+    return [("seeded N(0,1)", (q, k, v)), ("8 significant bits", tuple(fewer_bits(t) for t in (q, k, v))),
+            ("signed powers of two", tuple(pow2(t) for t in (q, k, v))),
+            ("zeros", tuple(torch.zeros_like(t) for t in (q, k, v)))]
+
+
+def smi_sample():
+    """Socket power (W) and the graphics clock of every XCD (MHz) from
+    `amd-smi metric -p -c --json`, or None where the tool or a field is
+    missing."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True, text=True, timeout=20)
+        d = json.loads(r.stdout)
+    except (OSError, subprocess.SubprocessError, ValueError):
+        return None
+    g = d["gpu_data"][0] if isinstance(d, dict) and "gpu_data" in d else (d[0] if isinstance(d, list) else d)
+    try:
+        watts = float(g["power"]["socket_power"]["value"])
+        clks = [float(c["clk"]["value"]) for n, c in g["clock"].items()
+                if n.startswith("gfx_") and isinstance(c, dict) and isinstance(c.get("clk"), dict)]
+    except (KeyError, TypeError, ValueError):
+        return None
+    return watts, clks
+
+
+def power_trace(w, inputs, seconds: float = 6.0):
+    """Socket power and XCD clocks while the kernel runs back to back for
+    about `seconds` on each input case of `input_cases` (two passes, so that
+    drift over the run shows): `amd-smi` is sampled from a second thread once
+    the first 2 s have passed.  One JSON line per case, to stderr."""
+    import threading
+    q, k, v = inputs
+    stream = torch.cuda.current_stream()
+    out = torch.empty(q.shape, dtype=torch.bfloat16 if w.dtype == "f8" else q.dtype, device=q.device)
+    lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=q.device)
+    for pass_no, (name, (a, b, c)) in [(p, nc) for p in (1, 2) for nc in input_cases(q, k, v)]:
+        def call():
+            attn.forward(a, b, c, causal=w.causal, window=w.window, scale=w.scale, out=out, lse=lse, stream=stream)
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        steps = max(10, int(seconds * 1e3 / max(e0.elapsed_time(e1), 1e-3)))
+        samples, stop = [], threading.Event()
+
+        def sampler():
+            if stop.wait(2.0):
+                return
+            while not stop.is_set():
+                smp = smi_sample()
+                if smp is not None:
+                    samples.append(smp)
+                stop.wait(0.5)
+        th = threading.Thread(target=sampler)
+        th.start()
+        e0.record(stream)
+        for _ in range(steps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        stop.set()
+        th.join()
+        ms = e0.elapsed_time(e1) / steps
+        tf = algorithmic_flops(w) / (ms * 1e-3) / 1e12
+        rec = {"power": name, "pass": pass_no, "workload": w.name, "steps": steps, "ms": round(ms, 4),
+               "tflops": round(tf, 1), "pct_of_mfma_peak": round(100 * tf / mfma_peak(w), 2), "samples": len(samples)}
+        if samples:
+            rec["socket_power_w_median"] = float(np.median([s[0] for s in samples]))
+            clks = [c for s in samples for c in s[1]]
+            if clks:
+                rec["gfx_clock_mhz_median"] = float(np.median(clks))
+                rec["gfx_clock_mhz_range"] = [min(clks), max(clks)]
+        print(json.dumps(rec), file=sys.stderr, flush=True)
+
+
 def data_sensitivity(w, inputs, steps: int):
     """The same kernel on the same shape with inputs whose values carry fewer
     significant bits: the seeded N(0,1) inputs, those values rounded to 8
@@ -157,17 +249,7 @@ def data_sensitivity(w, inputs, steps: int):
     power on operands with fewer bits set.  One JSON line per case, to stderr."""
     q, k, v = inputs
     dt = q.dtype
-
-    def fewer_bits(t):  # bf16 and fp8 values have 8 or fewer significant bits already
-        return t.to(torch.bfloat16).to(dt) if dt == torch.float16 else t
-
-    def pow2(t):
-        f = t.float()
-        return (torch.sign(f) * torch.exp2(torch.round(torch.log2(f.abs().clamp(min=2.0 ** -14))))).to(dt)
-
-    cases = [("seeded N(0,1)", (q, k, v)), ("8 significant bits", tuple(fewer_bits(t) for t in (q, k, v))),
-             ("signed powers of two", tuple(pow2(t) for t in (q, k, v))),
-             ("zeros", tuple(torch.zeros_like(t) for t in (q, k, v)))]
+    cases = input_cases(q, k, v)
     stream = torch.cuda.current_stream()
     out = torch.empty(q.shape, dtype=torch.bfloat16 if w.dtype == "f8" else dt, device=q.device)
     lse = torch.empty((w.B, w.H, w.L), dtype=torch.float32, device=q.device)
@@ -538,6 +620,9 @@ def main():
                          "'OOM' where standard attention ran out of memory) to this CSV file")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (attn_bwd) on the workload instead of the forward")
+    ap.add_argument("--power", action="store_true",
+                    help="also run the forward for ~6 s on each input case of --data-sensitivity while sampling "
+                         "socket power and XCD clocks with amd-smi; one JSON line per case (to stderr)")
     ap.add_argument("--torch-flash", action="store_true",
                     help="also time PyTorch's fused attention (FlashAttention backend) on the same inputs, "
                          "forward or backward; one JSON line to stderr")
@@ -604,6 +689,8 @@ def main():
         data_sensitivity(w, r["inputs"], max(5, args.steps))
     if args.torch_flash and w.dtype in ("f16", "bf16"):
         torch_flash(w, r["inputs"], args.steps, args.warmup, False, r["ms"])
+    if args.power:
+        power_trace(w, r["inputs"])
 
     r = line = None  # the headline's tensors are no longer needed
     torch.cuda.empty_cache()

@@ -24,7 +24,12 @@
 //      (16 contiguous bytes per lane), the V tile goes into LDS by
 //      direct-to-LDS loads (for the transposing read of the second product),
 //      both one tile ahead and the page-table entries two tiles ahead; the
-//      online softmax is per lane.
+//      online softmax is per lane.  When every V row is read by one wave only
+//      (one row block per K/V head) and the waves have long runs, the V loads
+//      carry the non-temporal hint: each one covers whole 128-byte lines, and
+//      streaming them past L2 raised the read rate by about a tenth.  The K
+//      loads keep the default policy: each covers 32 bytes of 32 rows, and
+//      the tile's other loads need those lines to stay in L2.
 //   2. merge: one workgroup per query row combines the partial results of the
 //      waves that touched its segment exactly (the same rescale the online
 //      softmax uses) and writes O and lse.
@@ -42,6 +47,16 @@
 #include "attn_common.h"
 
 namespace {
+
+// One 16-byte direct-to-LDS load per lane (as copy_to_lds16), with the
+// non-temporal cache policy (bit 1 of the instruction's cache-policy field)
+// when STREAM is set.
+template <bool STREAM>
+__device__ __forceinline__ void copy_to_lds16_policy(__amdgpu_buffer_rsrc_t src, void *lds_dst, int src_offset)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (__attribute__((address_space(3))) void *)lds_dst, 16,
+                                             src_offset, 0, 0, STREAM ? 2 : 0);
+}
 
 constexpr int kDecWaves = 4;     // independent waves per workgroup (tiles: kDecTile keys)
 constexpr int kMaxDevices = 64;
@@ -132,7 +147,7 @@ __device__ __forceinline__ int64_t wave_prefix_sum(int64_t x, int lane)
 }
 
 // ---------------------------------------------------------------- 1. partial
-template <typename T, int D>
+template <typename T, int D, bool STREAM>
 __global__ __launch_bounds__(64 * kDecWaves) void attn_decode_partial_kernel(DecParams p)
 {
     typedef typename Vec8<T>::type vec8;
@@ -238,7 +253,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void attn_decode_partial_kernel(Dec
                 __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, valid * kRowBytes, 0x00020000);
 #pragma unroll
             for (int cc = 0; cc < kHalfCopies; ++cc)
-                copy_to_lds16(rv, stage + hf * 16 * kRowBytes + cc * 1024, ld_v[cc]);
+                copy_to_lds16_policy<STREAM>(rv, stage + hf * 16 * kRowBytes + cc * 1024, ld_v[cc]);
         }
     };
 
@@ -569,7 +584,7 @@ size_t decode_workspace_bytes(int64_t B, int64_t H, int64_t H_kv, int64_t Lq, in
 // once per device and kernel instance); 0 when the query fails.
 std::mutex g_capacity_mutex;
 
-template <typename T, int D>
+template <typename T, int D, bool STREAM>
 int resident_waves()
 {
     static int cached[kMaxDevices];
@@ -580,7 +595,8 @@ int resident_waves()
         int cus = 0, blocks = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &blocks, reinterpret_cast<const void *>(&attn_decode_partial_kernel<T, D>), 64 * kDecWaves, 0) !=
+                &blocks, reinterpret_cast<const void *>(&attn_decode_partial_kernel<T, D, STREAM>), 64 * kDecWaves,
+                0) !=
                 hipSuccess ||
             cus < 1 || blocks < 1)
             return 0;
@@ -589,17 +605,44 @@ int resident_waves()
     return cached[dev];
 }
 
-template <typename T, int D>
-hipError_t launch_decode(DecParams p, hipStream_t stream)
+// Whether the partial kernel's V loads stream past L2: only when each V row
+// has one reader (a single row block per K/V head) and the waves' runs are
+// long (at least kStreamTiles tiles each by the upper bound on the tile
+// list); short runs are bound by latency, and the hint cost them about 2 %.
+constexpr int64_t kStreamTiles = 16;
+inline bool decode_streams_v(const DecParams &p)
 {
-    const int resident = resident_waves<T, D>();
+    if (p.n_rowblk != 1) return false;
+    const int64_t keys = p.window >= 0 ? std::min<int64_t>(p.max_len, (int64_t)p.window + p.Lq) : p.max_len;
+    const int64_t tiles = (int64_t)p.B * p.nseg * ((keys + kDecTile - 1) / kDecTile + 1);
+    return tiles >= kStreamTiles * p.n_waves;
+}
+
+template <typename T, int D, bool STREAM>
+hipError_t launch_partial(DecParams &p, hipStream_t stream)
+{
+    const int resident = resident_waves<T, D, STREAM>();
     if (resident < 1) return hipErrorInvalidDevice;
     p.n_waves = std::min(p.n_waves, resident);  // n_slots keeps the workspace layout of the cap
     void *kargs[] = {&p};
     const int grid1 = (p.n_waves + kDecWaves - 1) / kDecWaves;
-    hipError_t err = hipLaunchKernel(reinterpret_cast<const void *>(&attn_decode_partial_kernel<T, D>),
-                                     dim3((unsigned)grid1), dim3(64 * kDecWaves), kargs, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void *>(&attn_decode_partial_kernel<T, D, STREAM>),
+                           dim3((unsigned)grid1), dim3(64 * kDecWaves), kargs, 0, stream);
+}
+
+template <typename T, int D>
+hipError_t launch_decode(DecParams p, hipStream_t stream)
+{
+    // decided on the resident wave count, which both instances share (same
+    // registers and LDS)
+    const int resident = resident_waves<T, D, false>();
+    if (resident < 1) return hipErrorInvalidDevice;
+    DecParams probe = p;
+    probe.n_waves = std::min(p.n_waves, resident);
+    hipError_t err = decode_streams_v(probe) ? launch_partial<T, D, true>(p, stream)
+                                             : launch_partial<T, D, false>(p, stream);
     if (err != hipSuccess) return err;
+    void *kargs[] = {&p};
     // a row has at most about n_waves / (B * nseg) + 1 partial results (fewer
     // when the sequences are shorter than max_seq_len)
     const int64_t rows_total = (int64_t)p.B * p.H * p.Lq;

@@ -28,7 +28,8 @@
 //       small ones, and for two large products that cancel.
 //   calibrate_gfx950 --read    HBM read rate of a plain kernel over 3.3 GB,
 //       the data read in 4 KiB blocks in order and in a random order (the
-//       access pattern of a paged KV cache).
+//       access pattern of a paged KV cache), with default and with
+//       non-temporal loads.
 //   calibrate_gfx950 --atomics fp32 atomic adds as an atomic dQ would issue
 //       them in the backward at causal L = 131072, H = 4, d = 64: one
 //       workgroup per 128-key block and head adds a 64 x 64 fp32 tile into dQ
@@ -583,8 +584,10 @@ static int run_fp8acc()
 
 // ------------------------------------------------------------------ HBM read rate
 // Wave w reads 4 KiB blocks order[w*per .. w*per+per-1] (entries past nblk
-// are skipped), 16 bytes per lane per load; one word per lane is written.
+// are skipped), 16 bytes per lane per load (each load 1 KiB contiguous);
+// one word per lane is written.  NT: the loads carry the non-temporal hint.
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+template <bool NT>
 __global__ __launch_bounds__(256) void read_blocks(const u32x4 *x, const int *order, int per, int nblk, unsigned *out)
 {
     const int w = blockIdx.x * 4 + threadIdx.x / 64, lane = threadIdx.x % 64;
@@ -595,7 +598,10 @@ __global__ __launch_bounds__(256) void read_blocks(const u32x4 *x, const int *or
         const int64_t blk = order[bi];
         u32x4 v[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = x[blk * 256 + u * 64 + lane];
+        for (int u = 0; u < 4; ++u) {
+            const u32x4 *src = x + blk * 256 + u * 64 + lane;
+            v[u] = NT ? __builtin_nontemporal_load(src) : *src;
+        }
 #pragma unroll
         for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].w;
     }
@@ -615,9 +621,11 @@ static int run_read()
     CHECK_HIP(hipMalloc(&order, sizeof(int) * nblk));
     CHECK_HIP(hipMemset(x, 1, (size_t)nblk * 4096));
     std::vector<int> h(nblk);
-    for (int pass = 0; pass < 2; ++pass) {
+    for (int pass = 0; pass < 4; ++pass) {
+        const bool nt = pass >= 2;
+        auto kernel = nt ? read_blocks<true> : read_blocks<false>;
         for (int i = 0; i < nblk; ++i) h[i] = i;
-        if (pass == 1) {  // seeded Fisher-Yates shuffle (64-bit LCG)
+        if (pass % 2 == 1) {  // seeded Fisher-Yates shuffle (64-bit LCG)
             unsigned long long st = 12345;
             for (int i = nblk - 1; i > 0; --i) {
                 st = st * 6364136223846793005ULL + 1442695040888963407ULL;
@@ -628,21 +636,22 @@ static int run_read()
             }
         }
         CHECK_HIP(hipMemcpy(order, h.data(), sizeof(int) * nblk, hipMemcpyHostToDevice));
-        hipLaunchKernelGGL(read_blocks, dim3(waves / 4), dim3(256), 0, 0, x, order, per, nblk, out);
+        hipLaunchKernelGGL(kernel, dim3(waves / 4), dim3(256), 0, 0, x, order, per, nblk, out);
         CHECK_HIP(hipDeviceSynchronize());
         hipEvent_t e0, e1;
         CHECK_HIP(hipEventCreate(&e0));
         CHECK_HIP(hipEventCreate(&e1));
         CHECK_HIP(hipEventRecord(e0));
         for (int r = 0; r < 10; ++r)
-            hipLaunchKernelGGL(read_blocks, dim3(waves / 4), dim3(256), 0, 0, x, order, per, nblk, out);
+            hipLaunchKernelGGL(kernel, dim3(waves / 4), dim3(256), 0, 0, x, order, per, nblk, out);
         CHECK_HIP(hipEventRecord(e1));
         CHECK_HIP(hipEventSynchronize(e1));
         float ms = 0;
         CHECK_HIP(hipEventElapsedTime(&ms, e0, e1));
         ms /= 10;
-        std::printf("read %.2f GB as 4 KiB blocks, %-6s order: %.3f ms  %.0f GB/s\n", nblk * 4096e-9,
-                    pass ? "random" : "linear", ms, nblk * 4096.0 / (ms * 1e-3) / 1e9);
+        std::printf("read %.2f GB as 4 KiB blocks, %-6s order, %-12s loads: %.3f ms  %.0f GB/s\n", nblk * 4096e-9,
+                    pass % 2 ? "random" : "linear", nt ? "non-temporal" : "default", ms,
+                    nblk * 4096.0 / (ms * 1e-3) / 1e9);
     }
     CHECK_HIP(hipFree(x));
     CHECK_HIP(hipFree(out));

@@ -166,12 +166,13 @@ def input_cases(q, k, v):
 
 
 def smi_sample():
-    """Socket power (W) and the graphics clock of every XCD (MHz) from
-    `amd-smi metric -p -c --json`, or None where the tool or a field is
-    missing."""
+    """Socket power (W), the graphics clock of every XCD (MHz) and the
+    hotspot temperature (C, None if not reported) from `amd-smi metric -p -c
+    -t --json`, or None where the tool or a power/clock field is missing."""
     import subprocess
     try:
-        r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True, text=True, timeout=20)
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c", "-t", "--json"], capture_output=True, text=True,
+                           timeout=20)
         d = json.loads(r.stdout)
     except (OSError, subprocess.SubprocessError, ValueError):
         return None
@@ -182,7 +183,11 @@ def smi_sample():
                 if n.startswith("gfx_") and isinstance(c, dict) and isinstance(c.get("clk"), dict)]
     except (KeyError, TypeError, ValueError):
         return None
-    return watts, clks
+    try:
+        hot = float(g["temperature"]["hotspot"]["value"])
+    except (KeyError, TypeError, ValueError):
+        hot = None
+    return watts, clks, hot
 
 
 def power_trace(w, inputs, seconds: float = 6.0):
@@ -236,6 +241,9 @@ def power_trace(w, inputs, seconds: float = 6.0):
             if clks:
                 rec["gfx_clock_mhz_median"] = float(np.median(clks))
                 rec["gfx_clock_mhz_range"] = [min(clks), max(clks)]
+            hots = [s[2] for s in samples if s[2] is not None]
+            if hots:
+                rec["hotspot_c_max"] = max(hots)
         print(json.dumps(rec), file=sys.stderr, flush=True)
 
 

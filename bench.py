@@ -868,6 +868,8 @@ def torch_flash(w, inputs, steps: int, warmup: int, backward: bool, ms_kernel: f
         return rec
     q, k, v = (t.detach().requires_grad_(backward) for t in inputs[:3])
     kw = dict(is_causal=w.causal, scale=w.scale, enable_gqa=w.H_kv != w.H)
+    steps = max(1, steps)
+    res = None
     try:
         with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
             if backward:

@@ -380,9 +380,10 @@ __global__ __launch_bounds__(64 * kDecWaves) void attn_decode_partial_kernel(Dec
     // loads only (vmcnt, in issue order: all but the kTileLoads newest); before
     // a copy reuses a stage, its reads of that stage have completed (lgkmcnt).
     // Every step issues one tile's loads whether or not a tile is left (past
-    // the end of the run it loads the tile just processed again, which is
-    // still in L2), so every path through the loop has the same loads in
-    // flight and the compiler's own waits stay as loose as the ones here.
+    // the end of the run it loads the tile just processed again: its K rows
+    // are still in L2, its V rows too unless they were streamed), so every
+    // path through the loop has the same loads in flight and the compiler's
+    // own waits stay as loose as the ones here.
     // At the top of each step c0 is tile f (in stage a), c1 tile f+1, c2 tile
     // f+2, pg0 and pg1 the page entries of c0 and c1.
     constexpr int kTileLoads = kDSteps + 2 * kHalfCopies;  // vector memory instructions per tile

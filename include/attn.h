@@ -37,8 +37,12 @@
  *
  * Ownership and behaviour:
  *   - Every tensor pointer is a DEVICE pointer owned by the caller, who
- *     allocates and frees it.  The library allocates no device memory, keeps
- *     no state between calls, and never synchronises.
+ *     allocates and frees it.  The library allocates no device memory and
+ *     never synchronises; it enqueues kernels only (no memory set or copy),
+ *     so a call can be captured into a HIP graph.  The only state kept
+ *     between calls is read-only after its first use: the paged decode's
+ *     resident-wave count per device, and attn_decode_noalloc's scratch
+ *     address per device.
  *   - stream is a hipStream_t (NULL = the default stream).  The call enqueues
  *     the kernel on it and returns; results are ready once the stream has
  *     reached that point.  Calls on different streams may run concurrently.

@@ -191,10 +191,11 @@ def smi_sample():
 
 
 def power_trace(w, inputs, seconds: float = 6.0):
-    """Socket power and XCD clocks while the kernel runs back to back for
-    about `seconds` on each input case of `input_cases` (two passes, so that
-    drift over the run shows): `amd-smi` is sampled from a second thread once
-    the first 2 s have passed.  One JSON line per case, to stderr."""
+    """Socket power, XCD clocks and hotspot temperature while the kernel runs
+    back to back for about `seconds` on each input case of `input_cases` (two
+    passes, so that drift over the run shows): `amd-smi` is sampled from a
+    second thread once the first 2 s have passed.  One JSON line per case, to
+    stderr."""
     import threading
     q, k, v = inputs
     stream = torch.cuda.current_stream()
@@ -630,7 +631,8 @@ def main():
                     help="time the backward pass (attn_bwd) on the workload instead of the forward")
     ap.add_argument("--power", action="store_true",
                     help="also run the forward for ~6 s on each input case of --data-sensitivity while sampling "
-                         "socket power and XCD clocks with amd-smi; one JSON line per case (to stderr)")
+                         "socket power, XCD clocks and hotspot temperature with amd-smi; one JSON line per case "
+                         "(to stderr)")
     ap.add_argument("--torch-flash", action="store_true",
                     help="also time PyTorch's fused attention (FlashAttention backend) on the same inputs, "
                          "forward or backward; one JSON line to stderr")

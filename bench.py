@@ -610,7 +610,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None, choices=sorted(WORKLOADS) + sorted(DECODE_WORKLOADS))
     ap.add_argument("--sweep", action="store_true",
-                    help="also time every workload and print one extra JSON line each (to stderr)")
+                    help="also time every workload and print one extra JSON line each (to stderr); with "
+                         "--backward every 16-bit workload's backward, with --decode every decode workload")
     ap.add_argument("--data-sensitivity", action="store_true",
                     help="also time the workload's kernel on inputs with fewer significant bits (same "
                          "shape, same instructions) and print one extra JSON line each (to stderr); "
@@ -972,6 +973,25 @@ def main_decode(w, args):
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_decode(w, r["out"], r["inputs"], args.cpu_budget)
     print(json.dumps(line), flush=True)
+    if args.sweep:
+        r = line = None
+        torch.cuda.empty_cache()
+        rows = []
+        for name, wd in DECODE_WORKLOADS.items():
+            rs = time_decode(wd, max(100, args.steps), 10)
+            nb = decode_bytes(wd)
+            rec = {"decode_sweep": name, "dtype": wd.dtype, "B": wd.B, "Lq": wd.Lq, "steps": max(100, args.steps),
+                   "ms": round(rs["ms"], 4), "gbs": round(nb / (rs["ms"] * 1e-3) / 1e9, 1),
+                   "pct_hbm_peak": round(100 * nb / (rs["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                   "algorithmic_bytes": nb}
+            rows.append(rec)
+            print(json.dumps(rec), file=sys.stderr, flush=True)
+            del rs
+            torch.cuda.empty_cache()
+        if args.csv:
+            write_csv(args.csv, ["workload", "dtype", "B", "Lq", "time_ms", "GB_per_s", "pct_hbm_peak", "bytes"],
+                      [[r_["decode_sweep"], r_["dtype"], r_["B"], r_["Lq"], r_["ms"], r_["gbs"], r_["pct_hbm_peak"],
+                        r_["algorithmic_bytes"]] for r_ in rows])
 
 
 def main_backward(w, args):
@@ -1009,6 +1029,29 @@ def main_backward(w, args):
         data_sensitivity_bwd(w, r["inputs"], max(3, args.steps // 4))
     if args.torch_flash:
         torch_flash(w, r["inputs"], args.steps, args.warmup, True, r["ms"])
+    if args.sweep:
+        r = line = None
+        torch.cuda.empty_cache()
+        rows = []
+        for name, ws in WORKLOADS.items():
+            if ws.dtype == "f8":
+                continue  # the backward takes 16-bit inputs
+            short = ws.L <= 32768
+            steps, warm = max(50 if short else 10, args.steps), 5 if short else 2
+            rs = time_backward(ws, steps, warm)
+            f = algorithmic_flops_bwd(ws)
+            rec = {"backward_sweep": name, "dtype": ws.dtype, "L": ws.L, "steps": steps, "warmup": warm,
+                   "ms": round(rs["ms"], 4), "tflops": round(f / (rs["ms"] * 1e-3) / 1e12, 2),
+                   "pct_peak": round(100 * f / (rs["ms"] * 1e-3) / 1e12 / MFMA_PEAK_F16_TFLOPS, 2),
+                   "peak_mem_call_bytes": rs["peak_mem_call"]}
+            rows.append(rec)
+            print(json.dumps(rec), file=sys.stderr, flush=True)
+            del rs
+            torch.cuda.empty_cache()
+        if args.csv:
+            write_csv(args.csv, ["workload", "dtype", "L", "time_ms", "tflops", "pct_peak", "mem_GB"],
+                      [[r_["backward_sweep"], r_["dtype"], r_["L"], r_["ms"], r_["tflops"], r_["pct_peak"],
+                        round(r_["peak_mem_call_bytes"] / 1e9, 6)] for r_ in rows])
 
 
 def data_sensitivity_bwd(w, inputs, steps: int):

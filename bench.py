@@ -994,6 +994,15 @@ def main_decode(w, args):
                         r_["algorithmic_bytes"]] for r_ in rows])
 
 
+def bwd_launches(w) -> int:
+    """Kernel launches of one attn_bwd call: prep, then dK/dV and dQ, which
+    share one launch at d=64 when both together have at most 9 workgroups
+    (128 rows each) per CU."""
+    n_blk = (w.L + 127) // 128
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return 2 if w.d == 64 and n_blk * w.B * (w.H_kv + w.H) <= 9 * cus else 3
+
+
 def main_backward(w, args):
     r = time_backward(w, args.steps, args.warmup)
     flops = algorithmic_flops_bwd(w)
@@ -1015,12 +1024,13 @@ def main_backward(w, args):
                    "d": w.d, "causal": w.causal, "window": w.window, "scale": w.scale,
                    "algorithmic_flops": flops, "pct_of_mfma_peak": round(100 * tflops / MFMA_PEAK_F16_TFLOPS, 2),
                    "peak_mem_call_bytes": r["peak_mem_call"], "algorithmic_bytes": algorithmic_bytes_bwd(w),
-                   "launches_per_step": 3},
+                   "launches_per_step": bwd_launches(w)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_F16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_F16_TFLOPS, 4),
                      "traffic": profiled_traffic(w, "attn_bwd", KERNEL_SOURCE_BWD),
                      "traffic_requests": profiled_request_traffic(w, "attn_bwd", KERNEL_SOURCE_BWD),
-                     "scope": "one attn_bwd call (prep, dK/dV and dQ kernels)"},
+                     "scope": "one attn_bwd call (prep, then dK/dV and dQ: one launch each, or one shared "
+                              "launch on short d=64 grids)"},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_bwd(w, r["dq"], r["inputs"], args.cpu_budget)
